@@ -1,0 +1,393 @@
+// C ABI of the library: argument validation, workspace layout, the layer's
+// step loop and HIP-graph plans. Declarations and semantics: include/rt_prefill.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "rt_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rt_status fail(rt_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+rt_status hip_fail(hipError_t e, const char* what) {
+    return fail(RT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_bytes(rt_dtype dt) { return dt == RT_BF16 ? 2 : 4; }
+
+// Largest power of two dividing t (t >= 1): the block size of step t
+// (reading note lshu.cn/news/403416, summary section 4.2).
+int32_t block_of(int32_t t) { return t & -t; }
+
+rt_status check_attn(const rt_attn_desc* d) {
+    if (!d) return fail(RT_ERR_INVALID_ARG, "descriptor is NULL");
+    if (d->batch <= 0 || d->seq_len <= 0 || d->n_heads <= 0 || d->head_dim <= 0)
+        return fail(RT_ERR_INVALID_ARG, "batch, seq_len, n_heads and head_dim must be positive");
+    if (d->dtype != RT_F32 && d->dtype != RT_BF16) return fail(RT_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
+    if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
+        return fail(RT_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", d->head_dim);
+    if (!std::isfinite(d->softmax_scale)) return fail(RT_ERR_INVALID_ARG, "softmax_scale must be finite");
+    const double elems = (double)d->batch * d->seq_len * d->n_heads * d->head_dim;
+    if (elems > 4.0e12) return fail(RT_ERR_UNSUPPORTED, "tensor too large");
+    return RT_OK;
+}
+
+rt_status check_layer(const rt_layer_desc* d) {
+    if (!d) return fail(RT_ERR_INVALID_ARG, "descriptor is NULL");
+    rt_status st = check_attn(&d->attn);
+    if (st != RT_OK) return st;
+    if (d->d_model != d->attn.n_heads * d->attn.head_dim)
+        return fail(RT_ERR_INVALID_ARG, "d_model %d != n_heads*head_dim %d", d->d_model,
+                    d->attn.n_heads * d->attn.head_dim);
+    if (d->d_ff <= 0) return fail(RT_ERR_INVALID_ARG, "d_ff must be positive");
+    if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return fail(RT_ERR_INVALID_ARG, "rms_eps must be >= 0");
+    if (!std::isfinite(d->residual_scale)) return fail(RT_ERR_INVALID_ARG, "residual_scale must be finite");
+    if (d->attn.dtype == RT_BF16 && (d->d_model % 128 || d->d_ff % 128))
+        return fail(RT_ERR_UNSUPPORTED, "bf16 layers need d_model and d_ff multiples of 128");
+    return RT_OK;
+}
+
+// Workspace layout of one layer forward (byte offsets, 256-aligned).
+struct Layout {
+    size_t q, ke, ve;     // [N][B][d] dtype: queries and ephemeral pairs, formed up front
+    size_t m, l, o;       // [N][B][H], [N][B][H], [N][B][H][dh] fp32: online-softmax state
+    size_t a;             // [B][d] dtype: attention output of the current position
+    size_t h;             // [B][d] fp32: residual stream after the attention branch
+    size_t g;             // [B][F] dtype: MLP hidden activation
+    size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
+    size_t total;
+};
+
+Layout layout_of(const rt_layer_desc* d) {
+    const size_t es = elem_bytes(d->attn.dtype);
+    const size_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, D = d->d_model, F = d->d_ff;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    L.q = take(N * B * D * es);
+    L.ke = take(N * B * D * es);
+    L.ve = take(N * B * D * es);
+    L.m = take(N * B * H * 4);
+    L.l = take(N * B * H * 4);
+    L.o = take(N * B * D * 4);
+    L.a = take(B * D * es);
+    L.h = take(B * D * 4);
+    L.g = take(B * F * es);
+    L.wq = take(D * D * es);
+    L.wk = take(D * D * es);
+    L.wv = take(D * D * es);
+    L.w1 = take(F * D * es);
+    L.total = off;
+    return L;
+}
+
+struct Launcher {
+    hipStream_t s;
+    bool debug;
+    rt_status check(hipError_t e, const char* what) {
+        if (e != hipSuccess) return hip_fail(e, what);
+        if (debug) {
+            e = hipStreamSynchronize(s);
+            if (e != hipSuccess) return hip_fail(e, what);
+        }
+        return RT_OK;
+    }
+};
+
+#define RT_TRY(expr)                    \
+    do {                                \
+        rt_status _st = (expr);         \
+        if (_st != RT_OK) return _st;   \
+    } while (0)
+
+rt_status check_layer_ptrs(const rt_layer_weights* w, const void* x, void* z, void* kc, void* vc, void* ws) {
+    if (!w) return fail(RT_ERR_INVALID_ARG, "weights is NULL");
+    const void* ps[] = {w->w_q, w->w_k, w->w_v, w->w_o, w->w_1, w->w_2, x, z, kc, vc, ws};
+    const char* names[] = {"w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "x", "z", "k_cache", "v_cache", "workspace"};
+    for (int i = 0; i < 11; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i])) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (((uintptr_t)ws & 255u) != 0) return fail(RT_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    if ((w->g_attn && !aligned16(w->g_attn)) || (w->g_mlp && !aligned16(w->g_mlp)))
+        return fail(RT_ERR_INVALID_ARG, "gains must be 16-byte aligned");
+    return RT_OK;
+}
+
+// Enqueue the whole layer forward on stream s (eager, or inside a capture).
+rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const void* x, void* z, void* kc,
+                        void* vc, void* ws, hipStream_t s, bool debug) {
+    using namespace rt;
+    const rt_dtype dt = d->attn.dtype;
+    const size_t es = elem_bytes(dt);
+    const int32_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, dh = d->attn.head_dim;
+    const int32_t D = d->d_model, F = d->d_ff;
+    const Layout L = layout_of(d);
+    char* base = (char*)ws;
+    void *q = base + L.q, *ke = base + L.ke, *ve = base + L.ve;
+    float *m = (float*)(base + L.m), *l = (float*)(base + L.l), *o = (float*)(base + L.o);
+    void *a = base + L.a, *g = base + L.g;
+    float* h = (float*)(base + L.h);
+    Launcher run{s, debug};
+
+    // gains folded into the projections that follow each RMS normalisation
+    const void *wq = w->w_q, *wk = w->w_k, *wv = w->w_v, *w1 = w->w_1;
+    if (w->g_attn) {
+        RT_TRY(run.check(launch_fold_gain(dt, w->w_q, w->g_attn, base + L.wq, D, D, s), "fold g_attn"));
+        RT_TRY(run.check(launch_fold_gain(dt, w->w_k, w->g_attn, base + L.wk, D, D, s), "fold g_attn"));
+        RT_TRY(run.check(launch_fold_gain(dt, w->w_v, w->g_attn, base + L.wv, D, D, s), "fold g_attn"));
+        wq = base + L.wq;
+        wk = base + L.wk;
+        wv = base + L.wv;
+    }
+    if (w->g_mlp) {
+        RT_TRY(run.check(launch_fold_gain(dt, w->w_1, w->g_mlp, base + L.w1, F, D, s), "fold g_mlp"));
+        w1 = base + L.w1;
+    }
+
+    // every query and ephemeral pair depends only on the input: one GEMM up front
+    GemmArgs gq{};
+    gq.A = x; gq.lda = D;
+    gq.W[0] = wq; gq.W[1] = wk; gq.W[2] = wv;
+    gq.C[0] = q; gq.C[1] = ke; gq.C[2] = ve;
+    gq.ldc = D; gq.seg_n = D; gq.eps = d->rms_eps;
+    gq.M = (int64_t)N * B; gq.N = 3 * D; gq.K = D;
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::QKV, gq, s), "qkv projection"));
+
+    const int64_t P = (int64_t)B * H;
+    const float sigma2 = d->attn.softmax_scale * kLog2eHost;
+    UpdateArgs u{};
+    u.q = q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve;
+    u.m = m; u.l = l; u.o = o; u.a_out = a; u.P = P; u.sigma2 = sigma2;
+    // position 1: empty state, a_1 is its own ephemeral value
+    u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
+    RT_TRY(run.check(launch_update(dt, dh, u, s), "finalize position 1"));
+
+    const size_t slab = (size_t)B * D * es;
+    for (int32_t t = 1; t <= N; ++t) {
+        const char* xt = (const char*)x + (size_t)(t - 1) * slab;
+        char* zt = (char*)z + (size_t)(t - 1) * slab;
+        char* kt = (char*)kc + (size_t)(t - 1) * slab;
+        char* vt = (char*)vc + (size_t)(t - 1) * slab;
+
+        GemmArgs go{};  // h = x_t + rho W_o a_t
+        go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
+        go.R = xt; go.ldr = D; go.rscale = d->residual_scale; go.M = B; go.N = D; go.K = D;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "output projection"));
+
+        GemmArgs g1{};  // g = GELU(W_1 RMS_mlp(h))
+        g1.A = h; g1.lda = D; g1.W[0] = w1; g1.C[0] = g; g1.ldc = F; g1.seg_n = F;
+        g1.eps = d->rms_eps; g1.M = B; g1.N = F; g1.K = D;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, g1, s), "mlp up"));
+
+        GemmArgs g2{};  // z_t = h + rho W_2 g
+        g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = zt; g2.ldc = D; g2.seg_n = D;
+        g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = B; g2.N = D; g2.K = F;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, g2, s), "mlp down"));
+
+        GemmArgs gk{};  // persistent pair of position t from the output z_t
+        gk.A = zt; gk.lda = D; gk.W[0] = wk; gk.W[1] = wv; gk.C[0] = kt; gk.C[1] = vt;
+        gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = B; gk.N = 2 * D; gk.K = D;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection"));
+
+        if (t < N) {
+            // blocked step t, finishing query t+1 into a (its last merge)
+            const int32_t b = block_of(t);
+            u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
+            u.init = (b == t); u.fin = 1;
+            RT_TRY(run.check(launch_update(dt, dh, u, s), "blocked update"));
+        }
+    }
+    return RT_OK;
+}
+
+}  // namespace
+
+struct rt_plan {
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+};
+
+extern "C" {
+
+const char* rt_last_error(void) { return g_last_error.c_str(); }
+
+rt_status rt_schedule_step(int32_t t, int32_t n, int32_t* kv_first, int32_t* kv_last, int32_t* q_first,
+                           int32_t* q_last) {
+    if (!kv_first || !kv_last || !q_first || !q_last) return fail(RT_ERR_INVALID_ARG, "output pointer is NULL");
+    if (n <= 0 || t < 1 || t > n) return fail(RT_ERR_INVALID_ARG, "need 1 <= t <= n (t=%d, n=%d)", t, n);
+    const int32_t b = block_of(t);
+    *kv_first = t - b + 1;
+    *kv_last = t;
+    *q_first = t + 1;
+    *q_last = (int64_t)t + b < (int64_t)n ? t + b : n;
+    return RT_OK;
+}
+
+rt_status rt_blocked_attn_update(const rt_attn_desc* desc, int32_t t, const void* q, const void* k, const void* v,
+                                 float* m, float* l, float* o, rt_stream_t stream) {
+    RT_TRY(check_attn(desc));
+    if (t < 1 || t > desc->seq_len) return fail(RT_ERR_INVALID_ARG, "t=%d outside 1..%d", t, desc->seq_len);
+    const void* ps[] = {q, k, v, m, l, o};
+    const char* names[] = {"q", "k", "v", "m", "l", "o"};
+    for (int i = 0; i < 6; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i]) && i != 3 && i != 4) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (((uintptr_t)m & 3u) || ((uintptr_t)l & 3u)) return fail(RT_ERR_INVALID_ARG, "m and l must be 4-byte aligned");
+    const int32_t N = desc->seq_len, b = block_of(t);
+    const int32_t nq = (b < N - t) ? b : N - t;
+    if (nq <= 0) return RT_OK;
+    rt::UpdateArgs u{};
+    u.q = q; u.k = k; u.v = v; u.m = m; u.l = l; u.o = o;
+    u.P = (int64_t)desc->batch * desc->n_heads;
+    u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = nq;
+    u.sigma2 = desc->softmax_scale * rt::kLog2eHost;
+    u.init = (b == t); u.fin = 0;
+    hipError_t e = rt::launch_update(desc->dtype, desc->head_dim, u, (hipStream_t)stream);
+    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_blocked_attn_update launch");
+}
+
+rt_status rt_finalize_step(const rt_attn_desc* desc, int32_t t, const void* q, const void* k_eph,
+                           const void* v_eph, const float* m, const float* l, const float* o, void* a_t,
+                           rt_stream_t stream) {
+    RT_TRY(check_attn(desc));
+    if (t < 1 || t > desc->seq_len) return fail(RT_ERR_INVALID_ARG, "t=%d outside 1..%d", t, desc->seq_len);
+    const void* ps[] = {q, k_eph, v_eph, a_t};
+    const char* names[] = {"q", "k_eph", "v_eph", "a_t"};
+    for (int i = 0; i < 4; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i])) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (t > 1) {
+        if (!m || !l || !o) return fail(RT_ERR_INVALID_ARG, "state is NULL");
+        if (!aligned16(o) || ((uintptr_t)m & 3u) || ((uintptr_t)l & 3u))
+            return fail(RT_ERR_INVALID_ARG, "state is misaligned");
+    }
+    rt::UpdateArgs u{};
+    u.q = q; u.k_eph = k_eph; u.v_eph = v_eph;
+    u.m = const_cast<float*>(m); u.l = const_cast<float*>(l); u.o = const_cast<float*>(o);
+    u.a_out = a_t;
+    u.P = (int64_t)desc->batch * desc->n_heads;
+    u.kv0 = 0; u.nkv = 0; u.q0 = t - 1; u.nq = 1;
+    u.sigma2 = desc->softmax_scale * rt::kLog2eHost;
+    u.init = (t == 1); u.fin = 1;
+    hipError_t e = rt::launch_update(desc->dtype, desc->head_dim, u, (hipStream_t)stream);
+    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_finalize_step launch");
+}
+
+rt_status rt_update_finalize_step(const rt_attn_desc* desc, int32_t t, const void* q, const void* k_eph,
+                                  const void* v_eph, const void* k, const void* v, float* m, float* l, float* o,
+                                  void* a_next, rt_stream_t stream) {
+    RT_TRY(check_attn(desc));
+    if (t < 1 || t >= desc->seq_len) return fail(RT_ERR_INVALID_ARG, "t=%d outside 1..%d", t, desc->seq_len - 1);
+    const void* ps[] = {q, k_eph, v_eph, k, v, m, l, o, a_next};
+    const char* names[] = {"q", "k_eph", "v_eph", "k", "v", "m", "l", "o", "a_next"};
+    for (int i = 0; i < 9; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i]) && i != 5 && i != 6) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (((uintptr_t)m & 3u) || ((uintptr_t)l & 3u)) return fail(RT_ERR_INVALID_ARG, "m and l must be 4-byte aligned");
+    const int32_t N = desc->seq_len, b = block_of(t);
+    rt::UpdateArgs u{};
+    u.q = q; u.k = k; u.v = v; u.k_eph = k_eph; u.v_eph = v_eph; u.m = m; u.l = l; u.o = o; u.a_out = a_next;
+    u.P = (int64_t)desc->batch * desc->n_heads;
+    u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
+    u.sigma2 = desc->softmax_scale * rt::kLog2eHost;
+    u.init = (b == t); u.fin = 1;
+    hipError_t e = rt::launch_update(desc->dtype, desc->head_dim, u, (hipStream_t)stream);
+    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_update_finalize_step launch");
+}
+
+size_t rt_layer_workspace_bytes(const rt_layer_desc* desc) {
+    if (check_layer(desc) != RT_OK) return 0;
+    return layout_of(desc).total;
+}
+
+rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w, const void* x, void* z,
+                           void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
+                           rt_stream_t stream) {
+    RT_TRY(check_layer(desc));
+    RT_TRY(check_layer_ptrs(w, x, z, k_cache, v_cache, workspace));
+    const size_t need = layout_of(desc).total;
+    if (workspace_bytes < need)
+        return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return enqueue_layer(desc, w, x, z, k_cache, v_cache, workspace, (hipStream_t)stream,
+                         (desc->flags & RT_FLAG_DEBUG_SYNC) != 0);
+}
+
+rt_status rt_layer_plan_create(const rt_layer_desc* desc, const rt_layer_weights* w, const void* x, void* z,
+                               void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes,
+                               rt_plan** plan) {
+    if (!plan) return fail(RT_ERR_INVALID_ARG, "plan is NULL");
+    *plan = nullptr;
+    RT_TRY(check_layer(desc));
+    RT_TRY(check_layer_ptrs(w, x, z, k_cache, v_cache, workspace));
+    const size_t need = layout_of(desc).total;
+    if (workspace_bytes < need)
+        return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    hipStream_t cs;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "capture stream");
+    rt_plan* p = new rt_plan();
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        delete p;
+        return hip_fail(e, "hipStreamBeginCapture");
+    }
+    rt_status st = enqueue_layer(desc, w, x, z, k_cache, v_cache, workspace, cs, false);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (st != RT_OK || e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        delete p;
+        return st != RT_OK ? st : hip_fail(e, "hipStreamEndCapture");
+    }
+    p->graph = graph;
+    e = hipGraphInstantiate(&p->exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        delete p;
+        return hip_fail(e, "hipGraphInstantiate");
+    }
+    *plan = p;
+    return RT_OK;
+}
+
+rt_status rt_layer_plan_launch(rt_plan* plan, rt_stream_t stream) {
+    if (!plan || !plan->exec) return fail(RT_ERR_INVALID_ARG, "plan is NULL");
+    hipError_t e = hipGraphLaunch(plan->exec, (hipStream_t)stream);
+    return e == hipSuccess ? RT_OK : hip_fail(e, "hipGraphLaunch");
+}
+
+void rt_layer_plan_destroy(rt_plan* plan) {
+    if (!plan) return;
+    if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
+    if (plan->graph) (void)hipGraphDestroy(plan->graph);
+    delete plan;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Host-side internal interfaces of the library (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rt_prefill.h"
+
+namespace rt {
+
+constexpr float kLog2eHost = 1.4426950408889634f;  // log2(e): scores are kept in base 2
+
+// One step of the blocked schedule applied to a contiguous range of query
+// rows, optionally finishing the first row of the range into a_out.
+// Row indices are 0-based (row r holds position r+1).
+struct UpdateArgs {
+    const void* q;      // [N][P][dh]
+    const void* k;      // [N][P][dh] persistent keys
+    const void* v;      // [N][P][dh] persistent values
+    const void* k_eph;  // [N][P][dh] (read only when fin)
+    const void* v_eph;  // [N][P][dh] (read only when fin)
+    float* m;           // [N][P]
+    float* l;           // [N][P]
+    float* o;           // [N][P][dh]
+    void* a_out;        // [P][dh] (written only when fin)
+    int64_t P;          // batch * n_heads
+    int32_t kv0;        // first KV row of the block
+    int32_t nkv;        // KV rows in the block (0: finalize only)
+    int32_t q0;         // first query row
+    int32_t nq;         // query rows
+    float sigma2;       // softmax_scale * log2(e)
+    int32_t init;       // state rows are initialised, not read (first touch)
+    int32_t fin;        // row q0 is finished into a_out and its state is not written
+};
+
+hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
+
+// C[M][N] = epilogue(A[M][K] * W^T), W given as up to 3 column segments of
+// seg_n rows each ([seg_n][K] row-major), outputs likewise split.
+enum : int { EPI_RMS = 1, EPI_GELU = 2, EPI_RESID = 4 };
+struct GemmArgs {
+    const void* A;      // [M][lda]
+    int64_t lda;
+    const void* W[3];   // [seg_n][K] each
+    void* C[3];         // [M][ldc] each
+    int64_t ldc;
+    int32_t seg_n;
+    const void* R;      // [M][ldr] residual, added as R + rscale * acc
+    int64_t ldr;
+    float rscale;
+    float eps;
+    int64_t M;
+    int32_t N, K;
+};
+// Kinds of GEMM, by operand/output element types.
+enum class GemmKind {
+    QKV,      // A = x (T), RMS, C = q|k'|v' (T)
+    WO,       // A = a (T), C = h (f32), R = x (T)
+    W1,       // A = h (f32), RMS + GELU, C = g (T)
+    W2,       // A = g (T), C = z (T), R = h (f32)
+    KV,       // A = z (T), RMS, C = k|v (T)
+};
+hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
+bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K);
+
+// W_out[r][c] = W[r][c] * g[c] (fold an RMS gain into the following projection).
+hipError_t launch_fold_gain(rt_dtype dt, const void* W, const float* g, void* W_out, int64_t rows, int cols,
+                            hipStream_t s);
+
+}  // namespace rt

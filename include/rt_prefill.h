@@ -1,0 +1,203 @@
+/*
+ * rt_prefill.h -- C ABI of the MI355X (gfx950) Recurrent Transformer prefill library.
+ *
+ * The library computes the forward pass of a Recurrent Transformer (RT)
+ * layer over a whole sequence (prefill / training forward), as defined on
+ * the Recurrent Transformer reading note (lshu.cn/news/403416):
+ *   - translated paper section 2.2 and summary section 2.2: queries and an
+ *     ephemeral key/value pair of position t come from the layer input x_t;
+ *     the persistent pair (k_t, v_t) that later positions attend to comes
+ *     from the layer output z_t, so pairs are revealed one position at a time;
+ *   - summary section 4.2 ("blocked schedule"): every query is formed up
+ *     front; each keeps an online-softmax state (running maximum m,
+ *     normaliser l, numerator o); when pair t is revealed, the pairs
+ *     t-b+1..t are applied to queries t+1..t+b, b the largest power of two
+ *     dividing t. The result equals the naive schedule up to rounding order.
+ *   - translated paper section 6.3 / summary section 5.3: tensors indexed by
+ *     position are stored position-major.
+ *
+ * Conventions shared by every entry point
+ *   - Positions are 1-based in the API (t = 1..seq_len), as on the pages.
+ *   - All tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *     16-byte aligned, in the layouts stated below (row-major, last index
+ *     fastest). N = seq_len, B = batch, H = n_heads, dh = head_dim,
+ *     d = H*dh = d_model, F = d_ff. "[N][B][H][dh]" is the same memory as
+ *     "[N][B][d]": head h of a row is columns h*dh .. h*dh+dh-1.
+ *   - Element type of every activation, weight and cache tensor is the
+ *     descriptor's dtype (fp32 or bf16). The online-softmax state is always
+ *     fp32. Accumulation is always fp32.
+ *   - Calls enqueue work on the given HIP stream (NULL = the default stream)
+ *     and return without waiting; a kernel fault surfaces at the caller's next
+ *     synchronisation (immediately with RT_FLAG_DEBUG_SYNC).
+ *   - Arguments are validated before any HIP call. Errors are returned as
+ *     rt_status, never thrown or aborted; rt_last_error() gives the text of
+ *     the calling thread's last error.
+ *   - The library allocates no device memory in any entry point except
+ *     rt_layer_plan_create (which owns only its captured HIP graph).
+ */
+#ifndef RT_PREFILL_H
+#define RT_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* rt_stream_t; /* hipStream_t */
+
+typedef enum {
+    RT_OK = 0,
+    RT_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, t out of range, misaligned pointer */
+    RT_ERR_UNSUPPORTED = 2,  /* valid but not implemented: head_dim not in {32, 64, 128}, odd sizes */
+    RT_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than rt_layer_workspace_bytes() */
+    RT_ERR_HIP = 4           /* a HIP runtime call failed; see rt_last_error() */
+} rt_status;
+
+typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
+
+/* flags of rt_layer_desc */
+#define RT_FLAG_DEBUG_SYNC 1u   /* synchronise and check after every launch (slow; for debugging) */
+
+/* Attention shape. softmax_scale multiplies every score <k, q> (the pages'
+ * operator has none, i.e. 1.0; workloads use 1/sqrt(head_dim)). */
+typedef struct {
+    int32_t batch, seq_len, n_heads, head_dim;
+    rt_dtype dtype;
+    float softmax_scale;
+} rt_attn_desc;
+
+/* Layer shape. d_model must equal n_heads*head_dim. rms_eps is the epsilon
+ * of both RMS normalisations, RMS(v) = g * v / sqrt(mean(v^2) + eps).
+ * residual_scale rho multiplies both residual branches (the pages use
+ * 1/sqrt(number of layers); 1.0 gives the plain pre-LN layer). */
+typedef struct {
+    rt_attn_desc attn;
+    int32_t d_model, d_ff;
+    float rms_eps, residual_scale;
+    uint32_t flags;
+} rt_layer_desc;
+
+/* Weights, device pointers in the descriptor's dtype, row-major [out][in]:
+ * W_q, W_k, W_v, W_o: [d][d]; W_1: [F][d]; W_2: [d][F]. The same W_k, W_v
+ * form the ephemeral pair (from x_t) and the persistent pair (from z_t).
+ * g_attn (RMS gain before Q/K/V) and g_mlp (RMS gain before the MLP) are
+ * fp32 [d], or NULL for a vector of ones. */
+typedef struct {
+    const void *w_q, *w_k, *w_v, *w_o, *w_1, *w_2;
+    const float *g_attn, *g_mlp;
+} rt_layer_weights;
+
+/*
+ * rt_blocked_attn_update -- one step of the blocked schedule
+ * (reading note, summary section 4.2): with b = largest power of two dividing
+ * t, apply the persistent pairs of positions t-b+1..t to the online-softmax
+ * state of queries t+1..min(t+b, N).
+ *   q     [N][B][H][dh]  queries (dtype)
+ *   k, v  [N][B][H][dh]  persistent keys / values; rows t-b+1..t are read
+ *   m, l  [N][B][H]      fp32 state: running maximum of the base-2 logits
+ *                        s = softmax_scale*log2(e)*<k,q>, and sum of 2^(s-m)
+ *   o     [N][B][H][dh]  fp32 state: unnormalised numerator sum 2^(s-m) v
+ * State row j (position j) is read and written only by steps that cover
+ * query j. When t is a power of two the block starts at position 1, which
+ * is the first step to touch any of its queries: the state of those rows is
+ * then initialised, not read, so the caller never clears the state.
+ * t must be in 1..N; t = N (no query left) is a valid no-op.
+ */
+rt_status rt_blocked_attn_update(const rt_attn_desc* desc, int32_t t,
+                                 const void* q, const void* k, const void* v,
+                                 float* m, float* l, float* o, rt_stream_t stream);
+
+/*
+ * rt_finalize_step -- attention output of position t: merge the ephemeral
+ * pair (k'_t, v'_t) into query t's state and normalise, a_t = o / l
+ * (translated paper section 2.2: the ephemeral pair is used only by position
+ * t's own attention). At t = 1 the state is empty and a_1 = v'_1.
+ *   q, k_eph, v_eph [N][B][H][dh] (dtype); rows t are read
+ *   m, l [N][B][H], o [N][B][H][dh] (fp32): row t is read (not at t = 1), never written
+ *   a_t [B][H*dh] (dtype): written
+ * Call it after every update step t' < t has been enqueued.
+ */
+rt_status rt_finalize_step(const rt_attn_desc* desc, int32_t t,
+                           const void* q, const void* k_eph, const void* v_eph,
+                           const float* m, const float* l, const float* o,
+                           void* a_t, rt_stream_t stream);
+
+/*
+ * rt_update_finalize_step -- step t of the blocked schedule fused with the
+ * finalize of position t+1, in one launch: the pairs t-b+1..t are applied to
+ * queries t+1..min(t+b, N) as rt_blocked_attn_update does, except that query
+ * t+1, whose state is complete once step t is applied (every pair 1..t has
+ * then reached it), is finished into a_next = attention output of position
+ * t+1 (as rt_finalize_step(t+1) would) and its state row is not written.
+ * This is the update a layer forward runs after each position.
+ *   q, k_eph, v_eph, k, v [N][B][H][dh] (dtype); m, l [N][B][H], o [N][B][H][dh] (fp32)
+ *   a_next [B][H*dh] (dtype): written
+ * t must be in 1..N-1.
+ */
+rt_status rt_update_finalize_step(const rt_attn_desc* desc, int32_t t,
+                                  const void* q, const void* k_eph, const void* v_eph,
+                                  const void* k, const void* v,
+                                  float* m, float* l, float* o, void* a_next, rt_stream_t stream);
+
+/*
+ * rt_layer_workspace_bytes -- device workspace that rt_layer_forward and
+ * rt_layer_plan_create need for this shape, or 0 for an invalid descriptor.
+ */
+size_t rt_layer_workspace_bytes(const rt_layer_desc* desc);
+
+/*
+ * rt_layer_forward -- the RT layer x -> z over positions 1..N for B
+ * independent sequences (reading note, translated paper sections 2.1-2.2;
+ * the unit timed in the paper's section 6 is this single-layer map):
+ *   u_t = RMS_attn(x_t);  q_t, k'_t, v'_t = W_q u_t, W_k u_t, W_v u_t   (all t up front)
+ *   a_t = per-head softmax attention of q_t over persistent pairs 1..t-1
+ *         and the ephemeral pair t (blocked schedule)
+ *   h_t = x_t + rho W_o a_t
+ *   z_t = h_t + rho W_2 GELU(W_1 RMS_mlp(h_t))          (GELU with erf)
+ *   k_t, v_t = W_k RMS_attn(z_t), W_v RMS_attn(z_t)      (persistent pair)
+ *   x       [N][B][d]      input (dtype), read
+ *   z       [N][B][d]      output (dtype), written
+ *   k_cache [N][B][H][dh]  persistent keys (dtype), written: the KV cache a
+ *   v_cache [N][B][H][dh]  later decode step would read
+ *   workspace: device memory of at least rt_layer_workspace_bytes(desc),
+ *              256-byte aligned; its contents are scratch.
+ * The B sequences are independent (no exchange between batch rows).
+ */
+rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w,
+                           const void* x, void* z, void* k_cache, void* v_cache,
+                           void* workspace, size_t workspace_bytes, rt_stream_t stream);
+
+/*
+ * Plans: the same computation as rt_layer_forward, with its O(N) launches
+ * recorded once into a HIP graph and replayed by one launch (the paper's
+ * section 6.2 records its step loop as a CUDA graph for the same reason).
+ * The pointers given at creation are baked into the graph: the buffers must
+ * stay allocated, and keep their meaning, until rt_layer_plan_destroy.
+ * A plan may be launched any number of times, on any stream.
+ */
+typedef struct rt_plan rt_plan;
+rt_status rt_layer_plan_create(const rt_layer_desc* desc, const rt_layer_weights* w,
+                               const void* x, void* z, void* k_cache, void* v_cache,
+                               void* workspace, size_t workspace_bytes, rt_plan** plan);
+rt_status rt_layer_plan_launch(rt_plan* plan, rt_stream_t stream);
+void rt_layer_plan_destroy(rt_plan* plan);
+
+/*
+ * rt_schedule_step -- the integer rule of the blocked schedule on the host
+ * (reading note, summary section 4.2): for step t of an N-position sequence,
+ * the KV block [*kv_first, *kv_last] and the query block
+ * [*q_first, *q_last] (1-based, inclusive; empty when *q_first > *q_last).
+ * No HIP call.
+ */
+rt_status rt_schedule_step(int32_t t, int32_t n, int32_t* kv_first, int32_t* kv_last,
+                           int32_t* q_first, int32_t* q_last);
+
+/* Text of the calling thread's last error ("" if none). Never NULL. */
+const char* rt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RT_PREFILL_H */

@@ -57,6 +57,9 @@ def lib():
         L.rto_rmsnorm.argtypes = [_dp, ctypes.c_int, _fp, ctypes.c_double, _dp]
         L.rto_attention.restype = ctypes.c_int
         L.rto_attention.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_fp] * 5 + [_dp]
+        L.rto_attention_at.restype = ctypes.c_int
+        L.rto_attention_at.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_fp] * 5 + [
+            ctypes.c_int, ctypes.POINTER(ctypes.c_int), _dp]
         L.rto_layer_forward.restype = ctypes.c_int
         L.rto_layer_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _fp, ctypes.POINTER(_Out)]
         _lib = L
@@ -106,6 +109,20 @@ def attention(q, k_eph, v_eph, k, v, softmax_scale: float) -> np.ndarray:
     st = lib().rto_attention(N, R, H, dh, softmax_scale, *[p for _, p in arrs], out.ctypes.data_as(_dp))
     if st != 0:
         raise RuntimeError(f"rto_attention failed with status {st}")
+    return out
+
+
+def attention_at(q, k_eph, v_eph, k, v, softmax_scale: float, positions) -> np.ndarray:
+    """Naive RT attention of the listed 1-based positions only; returns [len(positions)][R][H][dh] float64."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    N, R, H, dh = q.shape
+    arrs = [_f32(t) for t in (q, k_eph, v_eph, k, v)]
+    sel = np.ascontiguousarray(positions, dtype=np.int32)
+    out = np.empty((len(sel), R, H, dh), dtype=np.float64)
+    st = lib().rto_attention_at(N, R, H, dh, softmax_scale, *[p for _, p in arrs], len(sel),
+                                sel.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), out.ctypes.data_as(_dp))
+    if st != 0:
+        raise RuntimeError(f"rto_attention_at failed with status {st}")
     return out
 
 

@@ -33,10 +33,13 @@
  *   - residual branches are multiplied by a residual scale rho (1/sqrt(L) in
  *     the paper's parameterisation, 1 in the workloads).
  * Arithmetic is IEEE double throughout (inputs arrive as fp32 values).
- * With round_bf16 set, the tensors that a bf16 implementation keeps in
- * memory between steps (q, k', v', the attention output, the MLP hidden
- * activation, z, and the persistent k, v) are rounded to the nearest bf16
+ * With round_bf16 set, every tensor that the bf16 implementation holds in
+ * bf16 between steps (q, k', v', the attention output, the MLP hidden
+ * activation, z, and the persistent k, v) is rounded to the nearest bf16
  * value, ties to even, and the rounded values are what later steps read.
+ * The residual stream h stays unrounded (it is kept in fp32), but the MLP's
+ * first product reads it as a bf16 operand: W_1 RMS(h) is formed as
+ * (W_1 bf16(h)) / rms(h), with rms taken from the unrounded h.
  * Reported outputs are the values BEFORE their own rounding.
  *
  * Parity of the whole layer is pinned only through its parts and special
@@ -81,13 +84,18 @@ void rto_rmsnorm(const double* x, int n, const float* g, double eps, double* out
 /* GELU with the exact Gaussian CDF. */
 double rto_gelu(double u) { return 0.5 * u * (1.0 + erf(u / sqrt(2.0))); }
 
-/* y[o] = sum_i W[o][i] u[i] for a row-major [n_out][n_in] matrix. */
-static void matvec(const float* W, const double* u, int n_out, int n_in, double* y) {
-    for (int o = 0; o < n_out; ++o) {
-        const float* w = W + (size_t)o * n_in;
-        double s = 0.0;
-        for (int i = 0; i < n_in; ++i) s += (double)w[i] * u[i];
-        y[o] = s;
+/* One weight row against R vectors: y[r*ys] = sum_i w[i] U[r*us + i], each sum
+ * taken in index order (rows go in chunks of 8 only so that the independent
+ * sums of different rows proceed side by side). */
+static void dot_rows(const float* w, int n_in, const double* U, size_t us, int R, double* y, size_t ys) {
+    for (int r0 = 0; r0 < R; r0 += 8) {
+        const int nr = R - r0 < 8 ? R - r0 : 8;
+        double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int i = 0; i < n_in; ++i) {
+            const double wi = (double)w[i];
+            for (int r = 0; r < nr; ++r) s[r] += wi * U[(size_t)(r0 + r) * us + i];
+        }
+        for (int r = 0; r < nr; ++r) y[(size_t)(r0 + r) * ys] = s[r];
     }
 }
 
@@ -173,6 +181,57 @@ int rto_attention(int n_pos, int n_rows, int n_heads, int head_dim, double sigma
     return status;
 }
 
+/*
+ * The same attention for selected positions only: a_sel[i] is the output of
+ * position sel[i] (1-based), [n_sel][n_rows][n_heads][head_dim]. Position t
+ * reads the persistent pairs 1..t-1 and its own ephemeral pair, so any
+ * position can be computed alone.
+ */
+int rto_attention_at(int n_pos, int n_rows, int n_heads, int head_dim, double sigma,
+                     const float* q, const float* k_eph, const float* v_eph,
+                     const float* k, const float* v, int n_sel, const int* sel, double* a_sel) {
+    if (n_pos < 0 || n_rows < 0 || n_heads <= 0 || head_dim <= 0 || head_dim > 512 || n_sel < 0) return RTO_BAD_ARG;
+    if (!q || !k_eph || !v_eph || !k || !v || !a_sel || (n_sel && !sel)) return RTO_BAD_ARG;
+    for (int i = 0; i < n_sel; ++i)
+        if (sel[i] < 1 || sel[i] > n_pos) return RTO_BAD_ARG;
+    const int d = n_heads * head_dim;
+    const size_t stride = (size_t)n_rows * d;
+    int status = RTO_OK;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int i = 0; i < n_sel; ++i) {
+        for (int p = 0; p < n_rows * n_heads; ++p) {
+            const int t = sel[i] - 1, r = p / n_heads, h = p % n_heads;
+            const size_t base = (size_t)r * d + (size_t)h * head_dim;
+            double* kk = malloc(sizeof(double) * ((size_t)t * head_dim + 1));
+            double* vv = malloc(sizeof(double) * ((size_t)t * head_dim + 1));
+            double* s = malloc(sizeof(double) * (size_t)(t + 1));
+            double qq[512], ke[512], ve[512];
+            if (!kk || !vv || !s) {
+#pragma omp atomic write
+                status = RTO_NO_MEMORY;
+            } else {
+                for (int j = 0; j < t; ++j)
+                    for (int e = 0; e < head_dim; ++e) {
+                        kk[(size_t)j * head_dim + e] = k[(size_t)j * stride + base + e];
+                        vv[(size_t)j * head_dim + e] = v[(size_t)j * stride + base + e];
+                    }
+                const size_t off = (size_t)t * stride + base;
+                for (int e = 0; e < head_dim; ++e) {
+                    qq[e] = q[off + e];
+                    ke[e] = k_eph[off + e];
+                    ve[e] = v_eph[off + e];
+                }
+                attend(qq, head_dim, sigma, kk, vv, head_dim, t, ke, ve, s,
+                       a_sel + (size_t)i * stride + base);
+            }
+            free(kk);
+            free(vv);
+            free(s);
+        }
+    }
+    return status;
+}
+
 /* ---- the layer ---------------------------------------------------------- */
 
 typedef struct {
@@ -248,13 +307,11 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
             rto_rmsnorm(xt, d, w->g_attn, eps, u);
         }
 #pragma omp parallel for schedule(static)
-        for (int p = 0; p < R * 3 * d; ++p) {
-            const int o = p / R, r = p % R, which = o / d, oo = o % d;
-            double* b = buf + r * per_row;
+        for (int o = 0; o < 3 * d; ++o) {
+            const int which = o / d, oo = o % d;
             const float* W = which == 0 ? w->w_q : (which == 1 ? w->w_k : w->w_v);
-            double s;
-            matvec(W + (size_t)oo * d, b + d, 1, d, &s);
-            b[2 * d + o] = s; /* q at 2d, k' at 3d, v' at 4d */
+            /* q at 2d, k' at 3d, v' at 4d of each row's scratch */
+            dot_rows(W + (size_t)oo * d, d, buf + d, per_row, R, buf + 2 * d + o, per_row);
         }
         /* 2. attention of position t over persistent pairs 1..t-1 plus its own ephemeral pair */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -279,35 +336,52 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
             for (int i = 0; i < d; ++i) b[9 * d + i] = keep(b[5 * d + i], rb);
         }
 #pragma omp parallel for schedule(static)
-        for (int p = 0; p < R * d; ++p) {
-            const int o = p / R, r = p % R;
-            double* b = buf + r * per_row;
-            double s;
-            matvec(w->w_o + (size_t)o * d, b + 9 * d, 1, d, &s);
-            b[6 * d + o] = b[o] + rho * s; /* h */
+        for (int o = 0; o < d; ++o) {
+            double s[256];
+            for (int r0 = 0; r0 < R; r0 += 256) {
+                const int nr = R - r0 < 256 ? R - r0 : 256;
+                dot_rows(w->w_o + (size_t)o * d, d, buf + (size_t)r0 * per_row + 9 * d, per_row, nr, s, 1);
+                for (int r = 0; r < nr; ++r) {
+                    double* b = buf + (size_t)(r0 + r) * per_row;
+                    b[6 * d + o] = b[o] + rho * s[r]; /* h */
+                }
+            }
         }
         /* 4. MLP on RMS_mlp(h): g = GELU(W_1 u2), z = h + rho W_2 g */
 #pragma omp parallel for schedule(static)
         for (int r = 0; r < R; ++r) {
             double* b = buf + r * per_row;
-            rto_rmsnorm(b + 6 * d, d, w->g_mlp, eps, b + 7 * d);
+            if (rb) {
+                /* RMS of the unrounded h; the product reads h rounded to bf16 */
+                double ss = 0.0;
+                for (int i = 0; i < d; ++i) ss += b[6 * d + i] * b[6 * d + i];
+                const double rr = 1.0 / sqrt(ss / d + eps);
+                for (int i = 0; i < d; ++i)
+                    b[7 * d + i] = (w->g_mlp ? (double)w->g_mlp[i] : 1.0) * rto_round_bf16(b[6 * d + i]) * rr;
+            } else {
+                rto_rmsnorm(b + 6 * d, d, w->g_mlp, eps, b + 7 * d);
+            }
         }
 #pragma omp parallel for schedule(static)
-        for (int p = 0; p < R * F; ++p) {
-            const int o = p / R, r = p % R;
-            double* b = buf + r * per_row;
-            double s;
-            matvec(w->w_1 + (size_t)o * d, b + 7 * d, 1, d, &s);
-            b[10 * d + o] = rto_gelu(s);              /* g before rounding */
-            b[10 * d + F + o] = keep(rto_gelu(s), rb); /* g as stored */
+        for (int o = 0; o < F; ++o) {
+            dot_rows(w->w_1 + (size_t)o * d, d, buf + 7 * d, per_row, R, buf + 10 * d + o, per_row);
+            for (int r = 0; r < R; ++r) {
+                double* b = buf + (size_t)r * per_row;
+                b[10 * d + o] = rto_gelu(b[10 * d + o]);      /* g before rounding */
+                b[10 * d + F + o] = keep(b[10 * d + o], rb);   /* g as stored */
+            }
         }
 #pragma omp parallel for schedule(static)
-        for (int p = 0; p < R * d; ++p) {
-            const int o = p / R, r = p % R;
-            double* b = buf + r * per_row;
-            double s;
-            matvec(w->w_2 + (size_t)o * F, b + 10 * d + F, 1, F, &s);
-            b[8 * d + o] = b[6 * d + o] + rho * s; /* z before rounding */
+        for (int o = 0; o < d; ++o) {
+            double s[256];
+            for (int r0 = 0; r0 < R; r0 += 256) {
+                const int nr = R - r0 < 256 ? R - r0 : 256;
+                dot_rows(w->w_2 + (size_t)o * F, F, buf + (size_t)r0 * per_row + 10 * d + F, per_row, nr, s, 1);
+                for (int r = 0; r < nr; ++r) {
+                    double* b = buf + (size_t)(r0 + r) * per_row;
+                    b[8 * d + o] = b[6 * d + o] + rho * s[r]; /* z before rounding */
+                }
+            }
         }
         /* 5. persistent pair of position t, from the stored output (or the input) */
 #pragma omp parallel for schedule(static)
@@ -322,18 +396,23 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
             rto_rmsnorm(zs, d, w->g_attn, eps, zs);
         }
 #pragma omp parallel for schedule(static)
-        for (int p = 0; p < R * 2 * d; ++p) {
-            const int o = p / R, r = p % R, oo = o % d;
-            double* b = buf + r * per_row;
-            double s;
-            matvec((o < d ? w->w_k : w->w_v) + (size_t)oo * d, b + 7 * d, 1, d, &s);
-            const size_t off = (size_t)t * Rd + (size_t)r * d + oo;
-            if (o < d) {
-                if (out->k) out->k[off] = s;
-                Kc[off] = keep(s, rb);
-            } else {
-                if (out->v) out->v[off] = s;
-                Vc[off] = keep(s, rb);
+        for (int o = 0; o < 2 * d; ++o) {
+            const int oo = o % d;
+            double s[256];
+            for (int r0 = 0; r0 < R; r0 += 256) {
+                const int nr = R - r0 < 256 ? R - r0 : 256;
+                dot_rows((o < d ? w->w_k : w->w_v) + (size_t)oo * d, d, buf + (size_t)r0 * per_row + 7 * d,
+                         per_row, nr, s, 1);
+                for (int r = 0; r < nr; ++r) {
+                    const size_t off = (size_t)t * Rd + (size_t)(r0 + r) * d + oo;
+                    if (o < d) {
+                        if (out->k) out->k[off] = s[r];
+                        Kc[off] = keep(s[r], rb);
+                    } else {
+                        if (out->v) out->v[off] = s[r];
+                        Vc[off] = keep(s[r], rb);
+                    }
+                }
             }
         }
         /* 6. report */

@@ -1,0 +1,158 @@
+"""The C-ABI library loads, exports what include/rt_prefill.h declares, and its
+host-side logic (schedule rule, argument validation, workspace sizing) behaves
+as documented -- all without a GPU (no call here reaches a HIP launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import blocked_prefill_amd as rt
+from oracle import schedule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rt.library_path):
+        from blocked_prefill_amd import build
+        build.build()
+    return rt.load()
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(rt_[a-z_0-9]+)\s*\(", text))
+    return names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert declared, "no declarations found"
+    assert declared == set(rt.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_library_is_hip_code_for_gfx950(lib):
+    blob = open(rt.library_path, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_host_schedule_matches_the_pages_rule(lib):
+    for n in (1, 2, 3, 7, 64, 100, 4096, 32768):
+        for t in list(range(1, min(n, 300) + 1)) + [n]:
+            assert rt.rt_schedule_step(t, n) == schedule.step(t, n), (t, n)
+
+
+def test_host_schedule_rejects_out_of_range(lib):
+    for t, n in [(0, 4), (5, 4), (1, 0), (-1, 8)]:
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_schedule_step(t, n)
+        assert e.value.status == 1
+
+
+def _attn(**kw):
+    d = dict(batch=2, seq_len=16, n_heads=2, head_dim=64, dtype=rt.RT_BF16, softmax_scale=0.125)
+    d.update(kw)
+    return rt.AttnDesc(**d)
+
+
+def _layer(**kw):
+    a = kw.pop("attn", _attn())
+    d = dict(attn=a, d_model=a.n_heads * a.head_dim, d_ff=256, rms_eps=1e-6, residual_scale=1.0, flags=0)
+    d.update(kw)
+    return rt.LayerDesc(**d)
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(seq_len=-3), 1), (dict(head_dim=48), 2), (dict(head_dim=256), 2),
+    (dict(dtype=7), 1), (dict(softmax_scale=float("inf")), 1),
+])
+def test_update_rejects_bad_descriptors(lib, kw, status):
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_blocked_attn_update(_attn(**kw), 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == status
+
+
+def test_update_rejects_bad_step_and_pointers(lib):
+    d = _attn()
+    for t in (0, 17):
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_blocked_attn_update(d, t, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+        assert e.value.status == 1 and "t=" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_blocked_attn_update(d, 3, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert "k is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_blocked_attn_update(d, 3, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert "aligned" in str(e.value)
+
+
+def test_update_at_last_position_is_a_noop(lib):
+    # t = N has no query left: valid, returns before any launch
+    rt.rt_blocked_attn_update(_attn(seq_len=16), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+
+
+def test_finalize_rejects_bad_arguments(lib):
+    d = _attn()
+    with pytest.raises(rt.RtError):
+        rt.rt_finalize_step(d, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_finalize_step(d, 2, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, stream=0)
+    assert "state" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_finalize_step(d, 1, FAKE, FAKE, FAKE, None, None, None, None, stream=0)
+    assert "a_t is NULL" in str(e.value)
+
+
+def test_workspace_bytes(lib):
+    d = _layer()
+    n, b, h, dh, f = 16, 2, 2, 64, 256
+    D = h * dh
+    al = lambda x: (x + 255) // 256 * 256
+    want = 3 * al(n * b * D * 2) + 2 * al(n * b * h * 4) + al(n * b * D * 4) + al(b * D * 2) + al(b * D * 4) \
+        + al(b * f * 2) + 3 * al(D * D * 2) + al(f * D * 2)
+    assert rt.rt_layer_workspace_bytes(d) == want
+    assert rt.rt_layer_workspace_bytes(_layer(d_model=100)) == 0
+    assert rt.rt_layer_workspace_bytes(_layer(d_ff=100)) == 0  # bf16 needs multiples of 128
+
+
+def test_layer_rejects_bad_arguments(lib):
+    d = _layer()
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    need = rt.rt_layer_workspace_bytes(d)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_forward(d, W, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, stream=0)
+    assert e.value.status == 3
+    W2 = dict(W, w_o=None)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_forward(d, W2, FAKE, FAKE, FAKE, FAKE, FAKE, need, stream=0)
+    assert "w_o is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_forward(d, W, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, stream=0)
+    assert "256-byte" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_forward(_layer(d_model=64), W, FAKE, FAKE, FAKE, FAKE, FAKE, need, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_plan_create(_layer(rms_eps=-1.0), W, FAKE, FAKE, FAKE, FAKE, FAKE, need)
+    assert e.value.status == 1
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    import importlib
+    mod = importlib.reload(rt)
+    monkeypatch.setattr(mod, "library_path", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(mod, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        mod.load()
+    importlib.reload(rt)

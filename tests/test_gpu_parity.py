@@ -1,0 +1,227 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU oracle.
+
+Every input is seeded and synthetic (rt_inputs). Small cases compare every
+element; the full-size workloads compare sampled batch rows (rows are
+independent) or sampled positions (the isolated attention of one position
+depends only on earlier inputs), at the shapes the bench times.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import rt_inputs
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    G.ensure_built()
+
+
+def _attn_case(seed, n, b, h, dh, dt):
+    w = rt_inputs.Workload("attn_case", b, n, h * dh, h, dh, 0, 0, dt, seed, update_only=True)
+    return rt_inputs.attn_inputs(w)
+
+
+# ---------------------------------------------------------------- attention update / finalize
+
+def test_first_position_is_its_ephemeral_value():
+    import torch
+    t = _attn_case(7, 4, 3, 2, 64, "bf16")
+    desc = G.attn_desc(3, 4, 2, 64, "bf16", 0.125)
+    q, ke, ve = (G.dev(t[n], "bf16") for n in ("q", "k_eph", "v_eph"))
+    a = torch.empty((3, 128), dtype=torch.bfloat16, device="cuda")
+    import blocked_prefill_amd as rt
+    rt.rt_finalize_step(desc, 1, q, ke, ve, None, None, None, a)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(3, 2, 64), ve[0])
+
+
+@pytest.mark.parametrize("dt,n,b,h,dh", [
+    ("bf16", 300, 3, 8, 64), ("bf16", 129, 2, 4, 128), ("bf16", 64, 5, 2, 32),
+    ("f32", 77, 2, 3, 32), ("f32", 65, 2, 2, 128), ("f32", 1, 2, 2, 64), ("bf16", 2, 1, 1, 64),
+])
+def test_update_sequence_matches_naive(dt, n, b, h, dh):
+    t = _attn_case(11 + n, n, b, h, dh, dt)
+    scale = 1.0 / math.sqrt(dh)
+    desc = G.attn_desc(b, n, h, dh, dt, scale)
+    a = G.run_attention_sequence(desc, *(G.dev(t[k], dt) for k in ("q", "k_eph", "v_eph", "k", "v")))
+    ref = oracle.attention(t["q"], t["k_eph"], t["v_eph"], t["k"], t["v"], scale)
+    G.parity(G.host(a), ref, dt, f"a[{dt},{n},{b},{h},{dh}]")
+
+
+def test_update_never_reads_stale_state():
+    """The state is never cleared by the caller: power-of-two steps initialise it."""
+    t = _attn_case(5, 100, 2, 2, 64, "bf16")
+    desc = G.attn_desc(2, 100, 2, 64, "bf16", 0.125)
+    args = [G.dev(t[k], "bf16") for k in ("q", "k_eph", "v_eph", "k", "v")]
+    a_nan = G.run_attention_sequence(desc, *args, state_fill=float("nan"))
+    a_zero = G.run_attention_sequence(desc, *args, state_fill=0.0)
+    assert np.array_equal(G.host(a_nan), G.host(a_zero))
+
+
+def test_update_full_size_sampled_rows():
+    """Isolated blocked update: B=64, 8 heads x 64, N=4096, bf16 inputs, fp32 state."""
+    w = rt_inputs.WORKLOADS["update_b64_n4096"]
+    t = rt_inputs.attn_inputs(w)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    desc = G.attn_desc(w.batch, w.n_pos, w.n_heads, w.head_dim, "bf16", scale)
+    a = G.run_attention_sequence(desc, *(G.dev(t[k], "bf16") for k in ("q", "k_eph", "v_eph", "k", "v")))
+    rows = [0, 1, 31, 63] + list(np.random.default_rng(0).choice(np.arange(2, 63), 2, replace=False))
+    ref = oracle.attention(*(t[k][:, rows] for k in ("q", "k_eph", "v_eph", "k", "v")), scale)
+    G.parity(G.host(a)[:, rows], ref, "bf16", "a (update, full size)")
+
+
+def test_update_long_sequence_sampled_positions():
+    """N = 32768 (B=8, 16 heads x 64): every block size up to 16384; sampled positions."""
+    n, b, h, dh = 32768, 8, 16, 64
+    t = _attn_case(1004, n, b, h, dh, "bf16")
+    scale = 1.0 / math.sqrt(dh)
+    desc = G.attn_desc(b, n, h, dh, "bf16", scale)
+    a = G.run_attention_sequence(desc, *(G.dev(t[k], "bf16") for k in ("q", "k_eph", "v_eph", "k", "v")))
+    pos = [1, 2, 3, 1024, 2049, 4097, 8193, 16385, 16386, 24577, 32767, 32768]
+    pos += [int(p) for p in np.random.default_rng(1).integers(4, n, 4)]
+    ref = oracle.attention_at(t["q"], t["k_eph"], t["v_eph"], t["k"], t["v"], scale, pos)
+    G.parity(G.host(a)[np.array(pos) - 1], ref, "bf16", "a (N=32768, sampled positions)")
+
+
+# ---------------------------------------------------------------- the layer
+
+def _small_weights(seed, d, f, dt, gains):
+    rng = np.random.default_rng(seed)
+    w = {
+        "w_q": rng.standard_normal((d, d)) / math.sqrt(d), "w_k": rng.standard_normal((d, d)) / math.sqrt(d),
+        "w_v": rng.standard_normal((d, d)) / math.sqrt(d), "w_o": rng.standard_normal((d, d)) / math.sqrt(d),
+        "w_1": rng.standard_normal((f, d)) / math.sqrt(d), "w_2": rng.standard_normal((d, f)) / math.sqrt(f),
+        "g_attn": (1 + 0.2 * rng.standard_normal(d)) if gains else np.ones(d),
+        "g_mlp": (1 + 0.2 * rng.standard_normal(d)) if gains else np.ones(d),
+    }
+    return {k: rt_inputs.to_storage(v.astype(np.float32), dt) if k.startswith("w") else v.astype(np.float32)
+            for k, v in w.items()}
+
+
+def _compare_layer(buf, x_rows, w_np, rows, dt, n_heads, scale, rho=1.0, what="layer"):
+    ref = oracle.layer_forward(x_rows, w_np, n_heads=n_heads, softmax_scale=scale, residual_scale=rho,
+                               round_bf16=(dt == "bf16"))
+    out = {}
+    for name, t in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
+        out[name] = G.parity(G.host(t)[:, rows], ref[name], dt, f"{what}.{name}")
+    return ref, out
+
+
+def test_layer_tiny_f32_all_rows():
+    """B=2, N=64, d=64, 2 heads x 32, MLP 256, fp32."""
+    wl = rt_inputs.WORKLOADS["tiny_f32"]
+    x = rt_inputs.layer_input(wl)
+    w = rt_inputs.layer_weights(wl, 0)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, "f32", scale)
+    buf = G.LayerBuffers(desc, G.dev(x, "f32"), w, "f32")
+    buf.forward()
+    _compare_layer(buf, x, w, list(range(wl.batch)), "f32", wl.n_heads, scale)
+
+
+@pytest.mark.parametrize("dt,n,b,d,h,f", [("f32", 50, 3, 96, 3, 128), ("bf16", 100, 5, 256, 4, 512),
+                                           ("bf16", 33, 2, 256, 2, 384)])
+def test_layer_small_with_gains_and_residual_scale(dt, n, b, d, h, f):
+    rng = np.random.default_rng(n)
+    x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), dt)
+    w = _small_weights(n + 1, d, f, dt, gains=True)
+    scale = 1.0 / math.sqrt(d // h)
+    desc = G.layer_desc(b, n, d, h, f, dt, scale, rho=0.7)
+    buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt, gains=True)
+    buf.forward()
+    # the library folds the gains into the projection weights, stored in the layer's dtype
+    w_fold = dict(w)
+    if dt == "bf16":
+        for n_, g in (("w_q", "g_attn"), ("w_k", "g_attn"), ("w_v", "g_attn"), ("w_1", "g_mlp")):
+            w_fold[n_] = rt_inputs.to_storage(w[n_] * w[g][None, :], dt)
+        w_fold["g_attn"] = None
+        w_fold["g_mlp"] = None
+    _compare_layer(buf, x, w_fold, list(range(b)), dt, h, scale, rho=0.7)
+
+
+def test_layer_plan_replays_match_eager():
+    import torch
+    n, b, d, h, f = 40, 3, 256, 4, 512
+    rng = np.random.default_rng(3)
+    x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), "bf16")
+    w = _small_weights(4, d, f, "bf16", gains=False)
+    desc = G.layer_desc(b, n, d, h, f, "bf16", 0.125)
+    buf = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16")
+    buf.forward()
+    torch.cuda.synchronize()
+    z0, k0, v0 = buf.z.clone(), buf.k.clone(), buf.v.clone()
+    plan = buf.plan()
+    for _ in range(3):
+        for t_ in (buf.z, buf.k, buf.v):
+            t_.fill_(float("nan"))
+        torch.cuda.synchronize()
+        plan.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.z, z0) and torch.equal(buf.k, k0) and torch.equal(buf.v, v0)
+    plan.destroy()
+
+
+def _full_layer(name, rows, use_plan=True):
+    import torch
+    wl = rt_inputs.WORKLOADS[name]
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    x = rt_inputs.layer_input(wl)
+    x_dev = G.dev(x, wl.dtype)
+    del x
+    x_rows = rt_inputs.layer_input(wl, rows=rows)
+    results = []
+    for layer in range(wl.n_layers):
+        w = rt_inputs.layer_weights(wl, layer)
+        desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, wl.dtype, scale)
+        buf = G.LayerBuffers(desc, x_dev, w, wl.dtype)
+        if use_plan:
+            p = buf.plan()
+            p.launch()
+            torch.cuda.synchronize()
+            p.destroy()
+        else:
+            buf.forward()
+            torch.cuda.synchronize()
+        ref, m = _compare_layer(buf, x_rows, w, rows, wl.dtype, wl.n_heads, scale, what=f"{name}[layer {layer}]")
+        results.append(m)
+        x_dev = buf.z            # the next layer reads this layer's stored output
+        x_rows = ref["x_next"]   # and the oracle its own stored output
+        del buf
+    return results
+
+
+def test_layer_full_d768_b512_n1024():
+    _full_layer("layer_d768_b512_n1024", rows=[0, 1, 255, 511])
+
+
+def test_stack_full_d1024_b512_n2048_six_layers():
+    _full_layer("stack6_d1024_b512_n2048", rows=[0, 511])
+
+
+def test_layer_long_b8_n32768_prefix():
+    """B=8, N=32768: the layer's positions 1..1024 of two rows (outputs there depend
+    only on earlier positions) plus finiteness of every output."""
+    import torch
+    wl = rt_inputs.WORKLOADS["long_d1024_b8_n32768"]
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    x = rt_inputs.layer_input(wl)
+    w = rt_inputs.layer_weights(wl, 0)
+    desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, "bf16", scale)
+    buf = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16")
+    buf.forward()
+    torch.cuda.synchronize()
+    for t_ in (buf.z, buf.k, buf.v):
+        assert bool(torch.isfinite(t_).all())
+    rows, T = [0, 7], 1024
+    ref = oracle.layer_forward(x[:T, rows], w, n_heads=wl.n_heads, softmax_scale=scale, round_bf16=True)
+    for name, t_ in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
+        G.parity(G.host(t_[:T])[:, rows], ref[name], "bf16", f"long.{name}")

@@ -138,6 +138,15 @@ def test_attention_ignores_pairs_at_or_after_own_position():
     assert not np.allclose(a[8:], a2[8:])
 
 
+def test_attention_at_selected_positions_equals_full():
+    rng = _rng(7)
+    t = _attn_tensors(rng, 40, 3, 2, 16)
+    full = oracle.attention(*t, 0.3)
+    sel = [40, 1, 17, 2, 33]
+    part = oracle.attention_at(*t, 0.3, sel)
+    assert np.array_equal(part, full[np.array(sel) - 1])
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 8, 37, 64])
 def test_attention_blocked_equals_naive(n):
     rng = _rng(10 + n)
