@@ -1,0 +1,231 @@
+"""Benchmark of the Recurrent Transformer prefill on one MI355X.
+
+One step = the forward pass x -> z of the whole 6-layer RT stack at B=512,
+N=2048, d_model=1024 (16 heads x 64), MLP 4096, bf16, over one batch of seeded
+synthetic input resident in HBM: per layer one HIP-graph replay of the whole
+step loop (up-front Q/K'/V' projection, then per position the fused blocked
+update + finalize, output projection, MLP, persistent K/V projection).
+
+Prints one JSON line. value = tokens/s of the stack (B*N tokens per step).
+roofline = the blocked-update kernel (the method's core, HBM-bound): its
+algorithmic bytes per launch over its average launch duration, timed with HIP
+events around each launch of one layer's update sequence on the launch stream.
+cpu_baseline = the CPU oracle (naive schedule, fp64) on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "RT layer prefill tokens/s at B=512 + blocked-update HBM GB/s / MFMA util"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def update_bytes(t, n, p, dh, s):
+    """Algorithmic HBM bytes of the fused update step t (1-based): KV block,
+    queries, state read (not on first touch) and write (not for the finished
+    row), and the finished row's ephemeral pair and output."""
+    b = t & -t
+    nq = min(b, n - t)
+    if nq <= 0:
+        return 0
+    kv = b * p * dh * s * 2
+    q = nq * p * dh * s
+    st_row = p * (dh + 2) * 4
+    reads = 0 if b == t else nq * st_row
+    writes = (nq - 1) * st_row
+    fin = 3 * p * dh * s
+    return kv + q + reads + writes + fin
+
+
+def update_flops(t, n, p, dh):
+    b = t & -t
+    nq = min(b, n - t)
+    return 4 * dh * b * nq * p + 4 * dh * p  # block scores + PV, plus the ephemeral pair
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack6_d1024_b512_n2048")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (batch rows are independent; "
+              "a multi-GPU run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import blocked_prefill_amd as rt
+    import rt_inputs
+
+    if not os.path.exists(rt.library_path):
+        from blocked_prefill_amd import build
+        build.build()
+    rt.load()
+
+    wl = rt_inputs.WORKLOADS[args.workload]
+    N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
+    scale = 1.0 / math.sqrt(dh)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    t0 = time.time()
+    x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
+    weights = []
+    for layer in range(L):
+        w = rt_inputs.layer_weights(wl, layer)
+        weights.append({n: torch.from_numpy(w[n]).to(torch.bfloat16).to(dev)
+                        for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")})
+    log(f"inputs generated and resident in HBM in {time.time() - t0:.1f}s")
+
+    attn = rt.AttnDesc(batch=B, seq_len=N, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=scale)
+    desc = rt.LayerDesc(attn=attn, d_model=D, d_ff=F, rms_eps=1e-6, residual_scale=1.0, flags=0)
+    ws_bytes = rt.rt_layer_workspace_bytes(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    zs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ks = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    vs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+
+    t0 = time.time()
+    plans = []
+    for layer in range(L):
+        xin = x if layer == 0 else zs[layer - 1]
+        plans.append(rt.rt_layer_plan_create(desc, weights[layer], xin, zs[layer], ks[layer], vs[layer], ws))
+    capture_s = time.time() - t0
+    log(f"captured {L} layer graphs in {capture_s:.2f}s")
+
+    def step():
+        for p in plans:
+            p.launch(stream)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.time()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    elapsed_ms = ev0.elapsed_time(ev1)
+    ms_per_step = elapsed_ms / args.steps
+    tokens_per_s = B * N * args.steps / (elapsed_ms / 1e3)
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms), "
+        f"{tokens_per_s / 1e6:.3f} M tokens/s")
+    assert bool(torch.isfinite(zs[-1]).all()), "non-finite output"
+
+    roofline = None
+    update_info = {}
+    if not args.no_kernel_timing:
+        # the last layer's q, k', v' and state are in the workspace, its caches in ks/vs:
+        # replay its update sequence (t = 1..N-1), one event pair per launch
+        base = ws.data_ptr()
+        es, al = 2, lambda v: (v + 255) // 256 * 256
+        off_q = 0
+        off_ke = off_q + al(N * B * D * es)
+        off_ve = off_ke + al(N * B * D * es)
+        off_m = off_ve + al(N * B * D * es)
+        off_l = off_m + al(N * B * H * 4)
+        off_o = off_l + al(N * B * H * 4)
+        a_next = torch.empty((B, D), dtype=torch.bfloat16, device=dev)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)]
+        torch.cuda.synchronize()
+        for t in range(1, N):
+            starts[t - 1].record(stream)
+            rt.rt_update_finalize_step(attn, t, base + off_q, base + off_ke, base + off_ve, ks[-1], vs[-1],
+                                       base + off_m, base + off_l, base + off_o, a_next, stream)
+            ends[t - 1].record(stream)
+        torch.cuda.synchronize()
+        durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+        P = B * H
+        byts = np.array([update_bytes(t, N, P, dh, 2) for t in range(1, N)], dtype=np.float64)
+        flops = np.array([update_flops(t, N, P, dh) for t in range(1, N)], dtype=np.float64)
+        avg_s = durs.mean() / 1e3
+        achieved = byts.mean() / avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "update_simt_kernel<bf16,64> (fused blocked update + finalize)",
+                    "launches": N - 1, "avg_launch_us": round(avg_s * 1e6, 2),
+                    "alg_bytes_per_launch": int(byts.mean())}
+        levels = {}
+        for t in range(1, N):
+            b = t & -t
+            lv = levels.setdefault(b, [0.0, 0.0, 0.0, 0])
+            lv[0] += durs[t - 1]
+            lv[1] += byts[t - 1]
+            lv[2] += flops[t - 1]
+            lv[3] += 1
+        update_info = {
+            "update_ms_per_layer": round(float(durs.sum()), 3),
+            "update_alg_GB_per_layer": round(float(byts.sum()) / 1e9, 3),
+            "per_level": {str(b): {"steps": v[3], "us_per_step": round(v[0] / v[3] * 1e3, 2),
+                                   "GB_s": round(v[1] / (v[0] / 1e3) / 1e9, 1),
+                                   "TFLOP_s": round(v[2] / (v[0] / 1e3) / 1e12, 2)}
+                          for b, v in sorted(levels.items())},
+        }
+        log(f"update kernel: {achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of HBM peak), "
+            f"{durs.sum():.2f} ms per layer")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        rows = list(range(args.cpu_rows))
+        xr = rt_inputs.layer_input(wl, rows=rows)
+        w0 = rt_inputs.layer_weights(wl, 0)
+        t0 = time.time()
+        oracle.layer_forward(xr, w0, n_heads=H, softmax_scale=scale, round_bf16=True)
+        cpu_s = time.time() - t0
+        # the sample is one of the stack's L layers: the stack rate is L times slower
+        cpu_value = len(rows) * N / (cpu_s * L)
+        cpu = {"value": round(cpu_value, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{len(rows)} batch rows x all {N} positions x layer 1 of {L} "
+                         f"({cpu_s:.1f} s); stack rate = rows*N/({L}*time)"}
+        log(f"cpu oracle: {cpu_s:.1f}s for the sample -> {cpu_value:.1f} stack tokens/s")
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) inputs, N(0,1/d_in) weights)",
+        "config": {"workload": f"{wl.name}: RT {L}-layer stack prefill x->z, bf16, B={B}, N={N}, d_model={D}, "
+                               f"{H} heads x {dh}, MLP {F} GELU",
+                   "batch": B, "seq_len": N, "layers": L, "ms_per_layer": round(ms_per_step / L, 3),
+                   "tokens_per_s_per_layer": round(tokens_per_s * L, 1), "graph_capture_s": round(capture_s, 2),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if update_info:
+        out["update"] = update_info
+    print(json.dumps(out), flush=True)
+    for p in plans:
+        p.destroy()
+
+
+if __name__ == "__main__":
+    main()

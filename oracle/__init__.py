@@ -51,6 +51,8 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         L.rto_round_bf16.restype = ctypes.c_double
         L.rto_round_bf16.argtypes = [ctypes.c_double]
+        L.rto_num_threads.restype = ctypes.c_int
+        L.rto_num_threads.argtypes = []
         L.rto_gelu.restype = ctypes.c_double
         L.rto_gelu.argtypes = [ctypes.c_double]
         L.rto_rmsnorm.restype = None
@@ -64,6 +66,11 @@ def lib():
         L.rto_layer_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _fp, ctypes.POINTER(_Out)]
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """Host threads the oracle uses."""
+    return int(lib().rto_num_threads())
 
 
 def _f32(a):

@@ -46,6 +46,7 @@
  * cases (no numeric worked example is printed on the pages).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -68,6 +69,9 @@ double rto_round_bf16(double v) {
     if (r > max_finite) r = INFINITY;
     return copysign(r, v);
 }
+
+/* Threads the oracle's parallel loops use. */
+int rto_num_threads(void) { return omp_get_max_threads(); }
 
 static double keep(double v, int round_bf16) { return round_bf16 ? rto_round_bf16(v) : v; }
 

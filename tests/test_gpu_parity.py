@@ -16,6 +16,11 @@ from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
+# Bound on the relative L2 distance between the GPU's own multi-layer chain and
+# the oracle's own chain (bf16 rounding-decision noise grows with depth; see
+# _full_layer). Each layer on identical inputs is held to the stated bars.
+CHAIN_DRIFT_REL_L2 = 2e-2
+
 
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
@@ -170,33 +175,67 @@ def test_layer_plan_replays_match_eager():
     plan.destroy()
 
 
+def _run_layer(desc, x_dev, w, dt, use_plan):
+    import torch
+    buf = G.LayerBuffers(desc, x_dev, w, dt)
+    if use_plan:
+        p = buf.plan()
+        p.launch()
+        torch.cuda.synchronize()
+        p.destroy()
+    else:
+        buf.forward()
+        torch.cuda.synchronize()
+    return buf
+
+
 def _full_layer(name, rows, use_plan=True):
+    """Full-size layer(s) in the bench's launch configuration (one HIP-graph
+    replay per layer), compared on sampled batch rows.
+
+    (1) Layer by layer on identical inputs: the sampled rows of the GPU layer's
+    input are the oracle's own stored output of the previous layer (rows are
+    independent, so the other rows cannot affect them); the layer's sampled
+    outputs must meet the bars.
+    (2) The GPU's own chain against the oracle's own chain: a bf16 recurrence
+    amplifies the noise of rounding decisions from layer to layer (two oracle
+    runs whose pre-rounding values differ by 1e-7 relative already disagree by
+    ~0.04 after two layers), so this drift is held to CHAIN_DRIFT_REL_L2."""
     import torch
     wl = rt_inputs.WORKLOADS[name]
+    dt = wl.dtype
     scale = 1.0 / math.sqrt(wl.head_dim)
-    x = rt_inputs.layer_input(wl)
-    x_dev = G.dev(x, wl.dtype)
-    del x
-    x_rows = rt_inputs.layer_input(wl, rows=rows)
-    results = []
+    chain_dev = G.dev(rt_inputs.layer_input(wl), dt)   # the GPU's own chain
+    x_rows = rt_inputs.layer_input(wl, rows=rows)      # the oracle's chain, sampled rows
+    idx = torch.tensor(rows, device="cuda")
+    per_layer, drift = [], []
     for layer in range(wl.n_layers):
         w = rt_inputs.layer_weights(wl, layer)
-        desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, wl.dtype, scale)
-        buf = G.LayerBuffers(desc, x_dev, w, wl.dtype)
-        if use_plan:
-            p = buf.plan()
-            p.launch()
-            torch.cuda.synchronize()
-            p.destroy()
+        desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, dt, scale)
+        ref = oracle.layer_forward(x_rows, w, n_heads=wl.n_heads, softmax_scale=scale, round_bf16=(dt == "bf16"))
+        xin = chain_dev.clone()
+        xin[:, idx] = G.dev(x_rows, dt)
+        same = _run_layer(desc, xin, w, dt, use_plan)
+        m = {nm: G.parity(G.host(t_[:, idx]), ref[nm], dt, f"{name}[layer {layer}].{nm}")
+             for nm, t_ in (("z", same.z), ("k", same.k), ("v", same.v))}
+        per_layer.append(m)
+        print(f"{name} layer {layer} on identical inputs: {m}")
+        if layer == 0:
+            chain_dev = same.z          # identical inputs at layer 0
         else:
-            buf.forward()
-            torch.cuda.synchronize()
-        ref, m = _compare_layer(buf, x_rows, w, rows, wl.dtype, wl.n_heads, scale, what=f"{name}[layer {layer}]")
-        results.append(m)
-        x_dev = buf.z            # the next layer reads this layer's stored output
-        x_rows = ref["x_next"]   # and the oracle its own stored output
-        del buf
-    return results
+            del same, xin
+            own = _run_layer(desc, chain_dev, w, dt, use_plan)
+            g = G.host(own.z[:, idx])
+            assert np.isfinite(g).all()
+            err = g - ref["z"]
+            c = {"rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref["z"])), "max_abs": float(np.abs(err).max())}
+            drift.append(c)
+            print(f"{name} layer {layer}, own chains: {c}")
+            assert c["rel_l2"] <= CHAIN_DRIFT_REL_L2, c
+            chain_dev = own.z
+            del own
+        x_rows = ref["x_next"]
+    return per_layer, drift
 
 
 def test_layer_full_d768_b512_n1024():
