@@ -97,6 +97,225 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
     }
 }
 
+// MFMA update for blocks of b >= 32 pairs, head_dim 64, bf16 (gfx950).
+//
+// A workgroup of WAVES waves takes one (batch*head pair p, tile of 32*WAVES
+// queries); each wave owns 32 queries. The block's keys and values stream
+// through LDS in tiles of 64 positions, shared by the waves:
+//   S^T[kv][q] = K Q^T       v_mfma_f32_32x32x16_bf16, A = K rows, B = Q^T
+//   O^T[dh][q] += V^T P^T    A = V^T (transposed into LDS), B = P^T
+// With K's rows fed in an order that swaps bits 2 and 3 of the row index,
+// the scores a lane holds for its query (lane % 32) cover 8 consecutive key
+// positions per 16-position slice, which is exactly the B-operand layout of
+// the second product: P never leaves registers, and the softmax statistics
+// and the O^T rescale are lane-local (the two lanes q and q+32 share a query).
+// Blocks are dispatched so that all query tiles of a pair land on the same
+// XCD back to back, keeping the pair's keys/values in that XCD's L2.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, int nqt) {
+    constexpr int DH = 64;
+    constexpr int KT = 64;          // key/value positions per LDS tile
+    constexpr int KSTR = DH + 8;    // bf16 per K row in LDS (16-byte pad)
+    constexpr int VSTR = KT + 8;    // bf16 per V^T row in LDS
+    constexpr int NT = 64 * WAVES;
+    __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KSTR];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[DH * VSTR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, ql = lane & 31;
+
+    int64_t pair;
+    int qtile;
+    {
+        const int64_t i = blockIdx.x;
+        if ((a.P & 7) == 0) {
+            const int64_t k = i >> 3;
+            pair = (k / nqt) * 8 + (i & 7);
+            qtile = (int)(k % nqt);
+        } else {
+            pair = i / nqt;
+            qtile = (int)(i % nqt);
+        }
+    }
+    const int64_t slab = a.P * DH;
+    const int wave_q0 = qtile * 32 * WAVES + wave * 32;
+    const bool wave_active = wave_q0 < a.nq;
+    const int qrow = wave_q0 + ql;
+    const bool qvalid = qrow < a.nq;
+    const int64_t j = (int64_t)a.q0 + qrow;
+
+    bf16x8 qop[4];
+    if (qvalid) {
+        const bf16* qp = (const bf16*)a.q + j * slab + pair * DH + 8 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qop[i] = *reinterpret_cast<const bf16x8*>(qp + 16 * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qop[i][e] = (bf16)0.f;
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16 o0, o1;  // O^T, dh 0..31 and 32..63
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        o0[e] = 0.f;
+        o1[e] = 0.f;
+    }
+    const bf16* kbase = (const bf16*)a.k + (int64_t)a.kv0 * slab + pair * DH;
+    const bf16* vbase = (const bf16*)a.v + (int64_t)a.kv0 * slab + pair * DH;
+    // this lane's K row within a 32-row chunk: bits 2 and 3 swapped
+    const int krow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
+    const float sigma2 = a.sigma2;
+
+    for (int kt0 = 0; kt0 < a.nkv; kt0 += KT) {
+        const int rows = (a.nkv - kt0) < KT ? (a.nkv - kt0) : KT;  // 32 or 64
+        __syncthreads();
+        for (int c = tid; c < rows * 8; c += NT) {
+            const int r = c >> 3, ch = (c & 7) * 8;
+            *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + ch]) =
+                *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
+        }
+        for (int c = tid; c < (rows / 2) * 8; c += NT) {
+            const int r0 = (c >> 3) * 2, ch = (c & 7) * 8;
+            const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch);
+            const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+                bf16x2 w;
+                w[0] = v0[i];
+                w[1] = v1[i];
+                *reinterpret_cast<bf16x2*>(&Vt[(ch + i) * VSTR + r0]) = w;
+            }
+        }
+        __syncthreads();
+        if (!wave_active) continue;
+        for (int c32 = 0; c32 < rows; c32 += 32) {
+            f32x16 s;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Ks[(c32 + krow) * KSTR + 16 * i + 8 * g]);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[i], s, 0, 0, 0);
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                s[e] *= sigma2;
+                mx = fmaxf(mx, s[e]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = fast_exp2(m_run - m_new);
+            float ps = 0.f;
+            bf16x8 p0, p1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pa = fast_exp2(s[e] - m_new);
+                const float pb = fast_exp2(s[e + 8] - m_new);
+                ps += pa + pb;
+                p0[e] = (bf16)pa;
+                p1[e] = (bf16)pb;
+            }
+            ps += __shfl_xor(ps, 32, 64);
+            l_run = l_run * alpha + ps;
+            m_run = m_new;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                o0[e] *= alpha;
+                o1[e] *= alpha;
+            }
+            const bf16* v_lo = &Vt[ql * VSTR + c32 + 8 * g];
+            const bf16* v_hi = &Vt[(32 + ql) * VSTR + c32 + 8 * g];
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_lo), p0, o0, 0, 0, 0);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_lo + 16), p1, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_hi), p0, o1, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_hi + 16), p1, o1, 0, 0, 0);
+        }
+    }
+    if (!qvalid) return;
+
+    // this lane holds dh = blk*32 + 8*ee + 4*g + (0..3) for blk in {0,1}, ee in 0..3 (accumulator e = 4*ee + i)
+    const int64_t sidx = j * a.P + pair;
+    float* orow = a.o + sidx * DH;
+    if (!a.init) {
+        const float ms = a.m[sidx], ls = a.l[sidx];
+        const float m_new = fmaxf(ms, m_run);
+        const float cs = fast_exp2(ms - m_new), cb = fast_exp2(m_run - m_new);
+        l_run = ls * cs + l_run * cb;
+        m_run = m_new;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+            const float4 s0 = *reinterpret_cast<const float4*>(orow + 8 * ee + 4 * g);
+            const float4 s1 = *reinterpret_cast<const float4*>(orow + 32 + 8 * ee + 4 * g);
+            o0[4 * ee + 0] = s0.x * cs + o0[4 * ee + 0] * cb;
+            o0[4 * ee + 1] = s0.y * cs + o0[4 * ee + 1] * cb;
+            o0[4 * ee + 2] = s0.z * cs + o0[4 * ee + 2] * cb;
+            o0[4 * ee + 3] = s0.w * cs + o0[4 * ee + 3] * cb;
+            o1[4 * ee + 0] = s1.x * cs + o1[4 * ee + 0] * cb;
+            o1[4 * ee + 1] = s1.y * cs + o1[4 * ee + 1] * cb;
+            o1[4 * ee + 2] = s1.z * cs + o1[4 * ee + 2] * cb;
+            o1[4 * ee + 3] = s1.w * cs + o1[4 * ee + 3] * cb;
+        }
+    }
+    if (a.fin && qrow == 0) {
+        // the position's own ephemeral pair (lanes 0 and 32 hold the two halves of the query)
+        const bf16* kp = (const bf16*)a.k_eph + j * slab + pair * DH + 8 * g;
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x8 kv = *reinterpret_cast<const bf16x8*>(kp + 16 * i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += (float)qop[i][e] * (float)kv[e];
+        }
+        d += __shfl_xor(d, 32, 64);
+        d *= sigma2;
+        const float m_new = fmaxf(m_run, d);
+        const float c = fast_exp2(m_run - m_new), pe = fast_exp2(d - m_new);
+        const float inv = 1.0f / (l_run * c + pe);
+        const bf16* vp = (const bf16*)a.v_eph + j * slab + pair * DH;
+        bf16* out = (bf16*)a.a_out + pair * DH;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int dh0 = blk * 32 + 8 * ee + 4 * g;
+                const bf16x4 ve = *reinterpret_cast<const bf16x4*>(vp + dh0);
+                bf16x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ov = blk ? o1[4 * ee + i] : o0[4 * ee + i];
+                    r[i] = (bf16)((ov * c + pe * (float)ve[i]) * inv);
+                }
+                *reinterpret_cast<bf16x4*>(out + dh0) = r;
+            }
+        }
+    } else {
+        if (g == 0) {
+            a.m[sidx] = m_run;
+            a.l[sidx] = l_run;
+        }
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+            *reinterpret_cast<float4*>(orow + 8 * ee + 4 * g) =
+                make_float4(o0[4 * ee + 0], o0[4 * ee + 1], o0[4 * ee + 2], o0[4 * ee + 3]);
+            *reinterpret_cast<float4*>(orow + 32 + 8 * ee + 4 * g) =
+                make_float4(o1[4 * ee + 0], o1[4 * ee + 1], o1[4 * ee + 2], o1[4 * ee + 3]);
+        }
+    }
+}
+
+template <int WAVES>
+static hipError_t launch_mfma(const UpdateArgs& a, hipStream_t s) {
+    const int nqt = (a.nq + 32 * WAVES - 1) / (32 * WAVES);
+    const int64_t blocks = a.P * nqt;
+    hipLaunchKernelGGL((update_mfma_kernel<WAVES>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a, nqt);
+    return hipGetLastError();
+}
+
 template <typename T, int DH>
 static hipError_t launch_simt(const UpdateArgs& a, hipStream_t s) {
     const int64_t threads = (int64_t)a.nq * a.P * (DH / 8);
@@ -116,7 +335,17 @@ static hipError_t launch_typed(int head_dim, const UpdateArgs& a, hipStream_t s)
     }
 }
 
+// Blocks of at least this many pairs go to the MFMA kernel (bf16, head_dim 64).
+constexpr int kMfmaMinBlock = 32;
+
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
+    if (a.nq <= 0) return hipSuccess;
+    if (dt == RT_BF16 && head_dim == 64 && a.nkv >= kMfmaMinBlock && (a.nkv % 32) == 0) {
+        const int waves_needed = (a.nq + 31) / 32;
+        if (waves_needed <= 1) return launch_mfma<1>(a, s);
+        if (waves_needed <= 2) return launch_mfma<2>(a, s);
+        return launch_mfma<4>(a, s);
+    }
     return dt == RT_BF16 ? launch_typed<bf16>(head_dim, a, s) : launch_typed<float>(head_dim, a, s);
 }
 

@@ -52,6 +52,7 @@ def test_first_position_is_its_ephemeral_value():
 @pytest.mark.parametrize("dt,n,b,h,dh", [
     ("bf16", 300, 3, 8, 64), ("bf16", 129, 2, 4, 128), ("bf16", 64, 5, 2, 32),
     ("f32", 77, 2, 3, 32), ("f32", 65, 2, 2, 128), ("f32", 1, 2, 2, 64), ("bf16", 2, 1, 1, 64),
+    ("bf16", 200, 3, 2, 64), ("bf16", 1000, 1, 1, 64), ("bf16", 513, 2, 4, 64),
 ])
 def test_update_sequence_matches_naive(dt, n, b, h, dh):
     t = _attn_case(11 + n, n, b, h, dh, dt)
