@@ -71,6 +71,8 @@ struct Layout {
     size_t a;             // [B][d] dtype: attention output of the current position
     size_t h;             // [B][d] fp32: residual stream after the attention branch
     size_t g;             // [B][F] dtype: MLP hidden activation
+    size_t hb;            // [B][d] bf16: h rounded, the MLP's first operand (bf16 layers)
+    size_t hss, zss;      // [d/32][B] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
     size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
     size_t total;
 };
@@ -94,6 +96,9 @@ Layout layout_of(const rt_layer_desc* d) {
     L.a = take(B * D * es);
     L.h = take(B * D * 4);
     L.g = take(B * F * es);
+    L.hb = take(B * D * 2);
+    L.hss = take(D / rt::kRowSSTile * B * 4 + 4);
+    L.zss = take(D / rt::kRowSSTile * B * 4 + 4);
     L.wq = take(D * D * es);
     L.wk = take(D * D * es);
     L.wv = take(D * D * es);
@@ -191,24 +196,34 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
         char* kt = (char*)kc + (size_t)(t - 1) * slab;
         char* vt = (char*)vc + (size_t)(t - 1) * slab;
 
+        // bf16 layers: W_o also stores h rounded to bf16 (the MLP's operand) and
+        // per-row partial sums of h^2; W_2 stores partial sums of z^2 (z as stored).
+        // The next GEMM turns those sums into its RMS row scale.
+        const bool b16 = dt == RT_BF16;
+        const int32_t parts = D / kRowSSTile;
+
         GemmArgs go{};  // h = x_t + rho W_o a_t
         go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
         go.R = xt; go.ldr = D; go.rscale = d->residual_scale; go.M = B; go.N = D; go.K = D;
+        if (b16) { go.C2 = base + L.hb; go.rss_out = (float*)(base + L.hss); }
         RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "output projection"));
 
         GemmArgs g1{};  // g = GELU(W_1 RMS_mlp(h))
-        g1.A = h; g1.lda = D; g1.W[0] = w1; g1.C[0] = g; g1.ldc = F; g1.seg_n = F;
-        g1.eps = d->rms_eps; g1.M = B; g1.N = F; g1.K = D;
+        g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = w1; g1.C[0] = g;
+        g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = B; g1.N = F; g1.K = D;
+        if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
         RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, g1, s), "mlp up"));
 
         GemmArgs g2{};  // z_t = h + rho W_2 g
         g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = zt; g2.ldc = D; g2.seg_n = D;
         g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = B; g2.N = D; g2.K = F;
+        if (b16) g2.rss_out = (float*)(base + L.zss);
         RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, g2, s), "mlp down"));
 
         GemmArgs gk{};  // persistent pair of position t from the output z_t
         gk.A = zt; gk.lda = D; gk.W[0] = wk; gk.W[1] = wv; gk.C[0] = kt; gk.C[1] = vt;
         gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = B; gk.N = 2 * D; gk.K = D;
+        if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
         RT_TRY(run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection"));
 
         if (t < N) {

@@ -8,10 +8,12 @@
 // epilogue. Section 2.1: the MLP is W_2 GELU(W_1 .) and both branches are
 // added to the residual stream, also fused here.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950, fp32 accumulation; tiles
-// staged global -> registers -> LDS with the next K tile prefetched into
-// registers while the current one is multiplied. fp32 path: plain SIMT,
-// one thread per output (used by small fp32 layers).
+// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950, fp32 accumulation, K tiles
+// prefetched several tiles ahead into registers and staged through a
+// double-buffered swizzled LDS tile. In bf16 layers the RMS sums of h and z
+// come from the producing GEMM's epilogue (per-row partial sums of the
+// stored values); the up-front projection sums its own A rows. fp32 path:
+// plain SIMT, one thread per output (used by small fp32 layers).
 #include "rt_device.h"
 #include "rt_internal.h"
 
@@ -28,60 +30,95 @@ __device__ __forceinline__ void epilogue_store(const GemmArgs& g, TC* C, int64_t
     C[row * g.ldc + (col % g.seg_n)] = from_f32<TC>(v);
 }
 
-// ---------------------------------------------------------------- bf16 MFMA
+// ---------------------------------------------------------------- bf16 MFMA, pipelined
 
-template <typename TA, typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
+// Workgroup barrier that orders LDS accesses only: global loads stay in
+// flight across it (a full __syncthreads would wait for every outstanding load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Slot of the 16-byte chunk c (0..7) of tile row r in LDS: rows of 128 bytes,
+// chunks XOR-swizzled by (r/2)%8 so that 16 consecutive rows read at one
+// chunk column fall in 16 different 4-bank groups.
+__device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+
+// C = epilogue(A * W^T) with A, W bf16 and K % 64 == 0, N % BN == 0.
+// K tiles of 64 are fetched into registers D tiles ahead of use (a ring of
+// D register stages, so D-1 tiles are in flight while one is multiplied),
+// written to a double-buffered swizzled LDS tile, and multiplied with
+// v_mfma_f32_32x32x16_bf16; each wave computes a (BM/WM) x (BN/WN) block.
+// One LDS-only barrier per K tile.
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     constexpr int NT = 64 * WM * WN;
     constexpr int BK = 64;
-    constexpr int LDS_STRIDE = BK + 8;          // bf16 elements per LDS row (16 B pad)
-    constexpr int TMW = BM / WM, TNW = BN / WN;  // wave tile
+    constexpr int TMW = BM / WM, TNW = BN / WN;
     constexpr int FM = TMW / 32, FN = TNW / 32;
-    constexpr int CA = BM * (BK / 8) / NT;       // 8-element A chunks per thread
-    constexpr int CW = BN * (BK / 8) / NT;
-    static_assert(CA >= 1 && CW >= 1 && FM >= 1 && FN >= 1, "tile too small for the workgroup");
-    static_assert(BM * (BK / 8) % NT == 0 && BN * (BK / 8) % NT == 0, "chunks must divide evenly");
+    constexpr int A_CH = BM * (BK / 8), W_CH = BN * (BK / 8);  // 16-byte chunks per tile
+    constexpr int LA = A_CH / NT, LW = W_CH / NT;               // chunks per thread per tile
+    constexpr int STAGE = (A_CH + W_CH) * 16;
+    static_assert(FM >= 1 && FN >= 1 && A_CH % NT == 0 && W_CH % NT == 0, "tile shape");
+    static_assert(D >= 2, "prefetch depth");
 
-    __shared__ bf16 As[BM * LDS_STRIDE];
-    __shared__ bf16 Ws[BN * LDS_STRIDE];
-    __shared__ float rs[BM];
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ float rs[BM];     // row scale (1/rms)
+    __shared__ float rsum[BM];   // row partial sums of squares of the stored output
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
+    const int gq = lane >> 5, l32 = lane & 31;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
     const int seg = n0 / g.seg_n;
     const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * g.K;
-    const TA* A = (const TA*)g.A;
+    const bf16* A = (const bf16*)g.A;
 
-    const int crow = tid / (BK / 8);  // first row this thread stages
-    const int ck = (tid % (BK / 8)) * 8;
-    constexpr int ROWS_PER_PASS = NT / (BK / 8);
-
-    bf16x8 ra[CA], rw[CW];
-    float ss[CA];
-#pragma unroll
-    for (int r = 0; r < CA; ++r) ss[r] = 0.f;
-
-    auto load_tiles = [&](int k0) {
-#pragma unroll
-        for (int r = 0; r < CA; ++r) {
-            const int64_t row = m0 + crow + r * ROWS_PER_PASS;
-            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (row < g.M) load8(A + row * g.lda + k0 + ck, v);
-            if (FLAGS & EPI_RMS) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss[r] += v[e] * v[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ra[r][e] = (bf16)v[e];
+    if (FLAGS & EPI_ROWSS)
+        for (int r = tid; r < BM; r += NT) rsum[r] = 0.f;
+    if (FLAGS & EPI_RMS_PARTS) {
+        for (int r = tid; r < BM; r += NT) {
+            const int64_t row = m0 + r;
+            float ss = 0.f;
+            if (row < g.M)
+                for (int p = 0; p < g.n_parts; ++p) ss += g.rss_in[(int64_t)p * g.M + row];
+            rs[r] = rsqrtf(ss / (float)g.K + g.eps);
         }
+    }
+
+    // this thread's chunks: slot s = NT*i + tid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
+    const bf16* a_src[LA];
+    int a_slot[LA];
 #pragma unroll
-        for (int r = 0; r < CW; ++r) {
-            const int row = crow + r * ROWS_PER_PASS;
-            rw[r] = *reinterpret_cast<const bf16x8*>(W + (int64_t)row * g.K + k0 + ck);
-        }
+    for (int i = 0; i < LA; ++i) {
+        const int s = NT * i + tid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+        int64_t row = m0 + r;
+        row = row < g.M ? row : g.M - 1;  // rows past M read a valid row; their results are dropped
+        a_src[i] = A + row * g.lda + c * 8;
+        a_slot[i] = s;
+    }
+    const bf16* w_src[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int s = NT * i + tid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+        w_src[i] = W + (int64_t)r * g.K + c * 8;
+    }
+
+    bf16x8 ra[D][LA], rw[D][LW];
+    auto load = [&](int u, int k0) {
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ra[u][i] = *reinterpret_cast<const bf16x8*>(a_src[i] + k0);
+#pragma unroll
+        for (int i = 0; i < LW; ++i) rw[u][i] = *reinterpret_cast<const bf16x8*>(w_src[i] + k0);
+    };
+    auto store = [&](int u, int buf) {
+        char* base = smem + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < LA; ++i) *reinterpret_cast<bf16x8*>(base + a_slot[i] * 16) = ra[u][i];
+#pragma unroll
+        for (int i = 0; i < LW; ++i) *reinterpret_cast<bf16x8*>(base + (A_CH + NT * i + tid) * 16) = rw[u][i];
     };
 
     f32x16 acc[FM][FN];
@@ -91,45 +128,72 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    float ss[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ss[i] = 0.f;
 
-    const int KT = g.K / BK;
-    load_tiles(0);
-    for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < CA; ++r)
-            *reinterpret_cast<bf16x8*>(&As[(crow + r * ROWS_PER_PASS) * LDS_STRIDE + ck]) = ra[r];
-#pragma unroll
-        for (int r = 0; r < CW; ++r)
-            *reinterpret_cast<bf16x8*>(&Ws[(crow + r * ROWS_PER_PASS) * LDS_STRIDE + ck]) = rw[r];
-        __syncthreads();
-        if (kt + 1 < KT) load_tiles((kt + 1) * BK);
+    auto compute = [&](int buf) {
+        const char* sA = smem + buf * STAGE;
+        const char* sW = sA + A_CH * 16;
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int kofs = kk * 16 + (lane >> 5) * 8;
+            const int c = 2 * kk + gq;
             bf16x8 aop[FM], wop[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-                aop[i] = *reinterpret_cast<const bf16x8*>(&As[(wm * TMW + i * 32 + (lane & 31)) * LDS_STRIDE + kofs]);
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * TMW + i * 32 + l32;
+                aop[i] = *reinterpret_cast<const bf16x8*>(sA + swz(r, c) * 16);
+                if ((FLAGS & EPI_RMS) && wn == 0) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-                wop[j] = *reinterpret_cast<const bf16x8*>(&Ws[(wn * TNW + j * 32 + (lane & 31)) * LDS_STRIDE + kofs]);
+                    for (int e = 0; e < 8; ++e) ss[i] += (float)aop[i][e] * (float)aop[i][e];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int r = wn * TNW + j * 32 + l32;
+                wop[j] = *reinterpret_cast<const bf16x8*>(sW + swz(r, c) * 16);
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], wop[j], acc[i][j], 0, 0, 0);
         }
+    };
+
+    // The K loop is branch-free so that the compiler's wait counts stay exact
+    // (the host guarantees KT % D == 0): prefetches past the last tile reload
+    // the last tile, and the one spare store lands in the LDS buffer nobody
+    // reads again.
+    const int KT = g.K / BK;
+    const int last = (KT - 1) * BK;
+    // prologue: tiles 0..D-1 in flight, tile 0 in LDS buffer 0, tile D replaces it in the ring
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(u, min(u * BK, last));
+    store(0, 0);
+    load(0, min(D * BK, last));
+    for (int kt0 = 0; kt0 < KT; kt0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int kt = kt0 + u;
+            lds_barrier();                 // tile kt is in LDS; tile kt-1's buffer is free
+            compute(kt & 1);
+            const int nu = (u + 1) % D;    // ring stage of tile kt+1 (constant once unrolled)
+            store(nu, (kt + 1) & 1);
+            load(nu, min((kt + 1 + D) * BK, last));
+        }
     }
 
     if (FLAGS & EPI_RMS) {
+        if (wn == 0) {
 #pragma unroll
-        for (int r = 0; r < CA; ++r) {
-            const float s = group_sum<BK / 8>(ss[r]);
-            if ((tid % (BK / 8)) == 0) rs[crow + r * ROWS_PER_PASS] = rsqrtf(s / (float)g.K + g.eps);
+            for (int i = 0; i < FM; ++i) {
+                const float s2 = ss[i] + __shfl_xor(ss[i], 32, 64);
+                if (gq == 0) rs[wm * TMW + i * 32 + l32] = rsqrtf(s2 / (float)g.K + g.eps);
+            }
         }
-        __syncthreads();
     }
+    if (FLAGS & (EPI_RMS | EPI_RMS_PARTS | EPI_ROWSS)) __syncthreads();
 
     TC* C = (TC*)g.C[seg];
 #pragma unroll
@@ -138,18 +202,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmArgs g) {
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                // 32x32 accumulator layout: lane holds column lane%32, rows 8*(e/4) + 4*(lane/32) + e%4
-                const int r = wm * TMW + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                const int c = wn * TNW + j * 32 + (lane & 31);
+                // 32x32 accumulator layout: column lane%32, row 8*(e/4) + 4*(lane/32) + e%4
+                const int r = wm * TMW + i * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
+                const int col = n0 + wn * TNW + j * 32 + l32;
                 const int64_t row = m0 + r;
-                if (row < g.M) epilogue_store<FLAGS, TR, TC>(g, C, row, n0 + c, acc[i][j][e], (FLAGS & EPI_RMS) ? rs[r] : 1.f);
+                if (row >= g.M) continue;
+                float v = acc[i][j][e];
+                if (FLAGS & (EPI_RMS | EPI_RMS_PARTS)) v *= rs[r];
+                if (FLAGS & EPI_GELU) v = gelu_erf(v);
+                if (FLAGS & EPI_RESID) v = to_f32(((const TR*)g.R)[row * g.ldr + col]) + g.rscale * v;
+                const TC out = from_f32<TC>(v);
+                C[row * g.ldc + (col % g.seg_n)] = out;
+                if (FLAGS & EPI_COPY) ((bf16*)g.C2)[row * g.ldc + (col % g.seg_n)] = (bf16)v;
+                if (FLAGS & EPI_ROWSS) {
+                    const float sv = to_f32(out);
+                    atomicAdd(&rsum[r], sv * sv);
+                }
             }
+    if (FLAGS & EPI_ROWSS) {
+        static_assert(!(FLAGS & EPI_ROWSS) || BN == kRowSSTile, "row partial sums assume the fixed tile width");
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) {
+            const int64_t row = m0 + r;
+            if (row < g.M) g.rss_out[(int64_t)blockIdx.x * g.M + row] = rsum[r];
+        }
+    }
 }
 
-template <typename TA, typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN>
-static hipError_t run_bf16(const GemmArgs& g, hipStream_t s) {
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D>
+static hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
     dim3 grid((uint32_t)(g.N / BN), (uint32_t)((g.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_bf16_kernel<TA, TC, TR, FLAGS, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, s, g);
+    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D>), grid, dim3(64 * WM * WN), 0, s, g);
     return hipGetLastError();
 }
 
@@ -185,7 +268,24 @@ static hipError_t run_f32(const GemmArgs& g, hipStream_t s) {
 bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0) return false;
     if (dt == RT_F32) return true;
-    return (K % 64 == 0) && (N % 64 == 0);
+    return (K % 64 == 0) && (N % 128 == 0);
+}
+
+template <int D>
+static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
+    const bool big = g.M >= 4096;
+    switch (kind) {
+        case GemmKind::QKV:
+            return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D>(g, s)
+                       : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D>(g, s);
+        case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
+            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D>(g, s);
+        case GemmKind::W1: return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 128, 2, 2, D>(g, s);
+        case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
+            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D>(g, s);
+        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D>(g, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s) {
@@ -199,17 +299,10 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
         }
         return hipErrorInvalidValue;
     }
-    const bool big = g.M >= 4096;
-    switch (kind) {
-        case GemmKind::QKV:
-            return big ? run_bf16<bf16, bf16, float, EPI_RMS, 128, 128, 2, 2>(g, s)
-                       : run_bf16<bf16, bf16, float, EPI_RMS, 64, 64, 2, 2>(g, s);
-        case GemmKind::WO: return run_bf16<bf16, float, bf16, EPI_RESID, 64, 64, 2, 2>(g, s);
-        case GemmKind::W1: return run_bf16<float, bf16, float, EPI_RMS | EPI_GELU, 64, 64, 2, 2>(g, s);
-        case GemmKind::W2: return run_bf16<bf16, bf16, float, EPI_RESID, 64, 64, 2, 2>(g, s);
-        case GemmKind::KV: return run_bf16<bf16, bf16, float, EPI_RMS, 64, 64, 2, 2>(g, s);
-    }
-    return hipErrorInvalidValue;
+    // K is a multiple of 128 (so the 64-wide K-tile count is even); prefetch 4 tiles ahead when it divides by 4
+    if ((g.K / 64) % 2) return hipErrorInvalidValue;
+    if ((g.K / 64) % 4 == 0) return dispatch_bf16<4>(kind, g, s);
+    return dispatch_bf16<2>(kind, g, s);
 }
 
 // ---------------------------------------------------------------- gain folding

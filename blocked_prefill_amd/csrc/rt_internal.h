@@ -37,7 +37,14 @@ hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStre
 
 // C[M][N] = epilogue(A[M][K] * W^T), W given as up to 3 column segments of
 // seg_n rows each ([seg_n][K] row-major), outputs likewise split.
-enum : int { EPI_RMS = 1, EPI_GELU = 2, EPI_RESID = 4 };
+enum : int {
+    EPI_RMS = 1,        // scale rows by 1/rms of the A row, summed by this kernel
+    EPI_GELU = 2,       // GELU (erf form)
+    EPI_RESID = 4,      // C = R + rscale * acc
+    EPI_RMS_PARTS = 8,  // scale rows by 1/rms from n_parts partial sums of squares (rss_in)
+    EPI_ROWSS = 16,     // write this tile's partial sum of squares of each stored row (rss_out)
+    EPI_COPY = 32,      // also store the result as bf16 into C2
+};
 struct GemmArgs {
     const void* A;      // [M][lda]
     int64_t lda;
@@ -51,7 +58,14 @@ struct GemmArgs {
     float eps;
     int64_t M;
     int32_t N, K;
+    const float* rss_in;  // [n_parts][M] (EPI_RMS_PARTS)
+    int32_t n_parts;
+    float* rss_out;       // [N / tile width][M] (EPI_ROWSS)
+    void* C2;             // [M][ldc] bf16 (EPI_COPY)
 };
+// Column-tile width of the GEMMs whose epilogue writes row partial sums
+// (the number of partial sums per row is N / this width).
+constexpr int kRowSSTile = 32;
 // Kinds of GEMM, by operand/output element types.
 enum class GemmKind {
     QKV,      // A = x (T), RMS, C = q|k'|v' (T)

@@ -120,7 +120,7 @@ def test_workspace_bytes(lib):
     D = h * dh
     al = lambda x: (x + 255) // 256 * 256
     want = 3 * al(n * b * D * 2) + 2 * al(n * b * h * 4) + al(n * b * D * 4) + al(b * D * 2) + al(b * D * 4) \
-        + al(b * f * 2) + 3 * al(D * D * 2) + al(f * D * 2)
+        + al(b * f * 2) + al(b * D * 2) + 2 * al(D // 32 * b * 4 + 4) + 3 * al(D * D * 2) + al(f * D * 2)
     assert rt.rt_layer_workspace_bytes(d) == want
     assert rt.rt_layer_workspace_bytes(_layer(d_model=100)) == 0
     assert rt.rt_layer_workspace_bytes(_layer(d_ff=100)) == 0  # bf16 needs multiples of 128
