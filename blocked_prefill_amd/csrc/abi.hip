@@ -61,6 +61,8 @@ rt_status check_layer(const rt_layer_desc* d) {
     if (!std::isfinite(d->residual_scale)) return fail(RT_ERR_INVALID_ARG, "residual_scale must be finite");
     if (d->attn.dtype == RT_BF16 && (d->d_model % 128 || d->d_ff % 128))
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers need d_model and d_ff multiples of 128");
+    if (d->attn.dtype == RT_BF16 && d->d_model > 64 * rt::kRowSSTile)
+        return fail(RT_ERR_UNSUPPORTED, "bf16 layers support d_model up to %d", 64 * rt::kRowSSTile);
     return RT_OK;
 }
 
@@ -72,7 +74,7 @@ struct Layout {
     size_t h;             // [B][d] fp32: residual stream after the attention branch
     size_t g;             // [B][F] dtype: MLP hidden activation
     size_t hb;            // [B][d] bf16: h rounded, the MLP's first operand (bf16 layers)
-    size_t hss, zss;      // [d/32][B] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
+    size_t hss, zss;      // [B][d/32] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
     size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
     size_t total;
 };

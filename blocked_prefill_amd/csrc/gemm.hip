@@ -14,12 +14,26 @@
 // come from the producing GEMM's epilogue (per-row partial sums of the
 // stored values); the up-front projection sums its own A rows. fp32 path:
 // plain SIMT, one thread per output (used by small fp32 layers).
+#include <type_traits>
+
 #include "rt_device.h"
 #include "rt_internal.h"
 
 namespace rt {
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(u) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-u^2),
+// t = 1/(1 + p u), u >= 0, absolute error <= 1.5e-7; odd extension for u < 0.
+__device__ __forceinline__ float erf_as(float u) {
+    const float a = fabsf(u);
+    const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * a);
+    const float poly =
+        t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+    const float e = __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+    return copysignf(1.0f - poly * e, u);
+}
+// GELU with the Gaussian CDF: x/2 (1 + erf(x/sqrt 2)).
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
 
 template <int FLAGS, typename TR, typename TC>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& g, TC* C, int64_t row, int64_t col, float v,
@@ -51,12 +65,17 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1)
 // written to a double-buffered swizzled LDS tile, and multiplied with
 // v_mfma_f32_32x32x16_bf16; each wave computes a (BM/WM) x (BN/WN) block.
 // One LDS-only barrier per K tile.
-template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D>
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
+    // MF = 32: v_mfma_f32_32x32x16_bf16 blocks; MF = 16: v_mfma_f32_16x16x32_bf16 blocks
+    // (four times as many independent accumulators for the same wave tile).
+    static_assert(MF == 32 || MF == 16, "MFMA block");
     constexpr int NT = 64 * WM * WN;
     constexpr int BK = 64;
     constexpr int TMW = BM / WM, TNW = BN / WN;
-    constexpr int FM = TMW / 32, FN = TNW / 32;
+    constexpr int FM = TMW / MF, FN = TNW / MF;
+    typedef typename std::conditional<MF == 32, f32x16, f32x4>::type acc_t;
+    constexpr int AE = MF == 32 ? 16 : 4;  // accumulator elements per lane
     constexpr int A_CH = BM * (BK / 8), W_CH = BN * (BK / 8);  // 16-byte chunks per tile
     constexpr int LA = A_CH / NT, LW = W_CH / NT;               // chunks per thread per tile
     constexpr int STAGE = (A_CH + W_CH) * 16;
@@ -69,22 +88,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
-    const int gq = lane >> 5, l32 = lane & 31;
+    const int gq = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
     const int seg = n0 / g.seg_n;
     const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * g.K;
     const bf16* A = (const bf16*)g.A;
 
-    if (FLAGS & EPI_ROWSS)
-        for (int r = tid; r < BM; r += NT) rsum[r] = 0.f;
+    // partial sums of squares of this tile's A rows (EPI_RMS_PARTS), laid out
+    // [M][n_parts] with n_parts % 4 == 0 and <= 64: fetched now as float4s,
+    // combined after the main loop.
+    constexpr int PQ = (BM * 16 + NT - 1) / NT;  // float4 quads per thread
+    float4 pss[(FLAGS & EPI_RMS_PARTS) ? PQ : 1];
+    const int qpr = g.n_parts / 4;                // quads per row
     if (FLAGS & EPI_RMS_PARTS) {
-        for (int r = tid; r < BM; r += NT) {
+#pragma unroll
+        for (int i = 0; i < PQ; ++i) {
+            const int idx = tid + NT * i, r = idx / qpr;
             const int64_t row = m0 + r;
-            float ss = 0.f;
-            if (row < g.M)
-                for (int p = 0; p < g.n_parts; ++p) ss += g.rss_in[(int64_t)p * g.M + row];
-            rs[r] = rsqrtf(ss / (float)g.K + g.eps);
+            pss[i] = (r < BM && row < g.M)
+                         ? reinterpret_cast<const float4*>(g.rss_in + row * g.n_parts)[idx % qpr]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
 
@@ -121,27 +145,31 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
         for (int i = 0; i < LW; ++i) *reinterpret_cast<bf16x8*>(base + (A_CH + NT * i + tid) * 16) = rw[u][i];
     };
 
-    f32x16 acc[FM][FN];
+    acc_t acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+            for (int e = 0; e < AE; ++e) acc[i][j][e] = 0.f;
     float ss[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) ss[i] = 0.f;
 
+    // operand fetch: lane holds 8 consecutive k of row (lane % MF), k-group lane / MF
+    const int lrow = lane % MF, lgrp = lane / MF;
     auto compute = [&](int buf) {
         const char* sA = smem + buf * STAGE;
         const char* sW = sA + A_CH * 16;
+        constexpr int KS = MF == 32 ? 16 : 32;  // k per MFMA
+        constexpr int GPS = KS / 8;             // 16-byte chunks per MFMA k-slice
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int c = 2 * kk + gq;
+        for (int kk = 0; kk < BK / KS; ++kk) {
+            const int c = GPS * kk + lgrp;
             bf16x8 aop[FM], wop[FN];
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const int r = wm * TMW + i * 32 + l32;
+                const int r = wm * TMW + i * MF + lrow;
                 aop[i] = *reinterpret_cast<const bf16x8*>(sA + swz(r, c) * 16);
                 if ((FLAGS & EPI_RMS) && wn == 0) {
 #pragma unroll
@@ -150,14 +178,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
             }
 #pragma unroll
             for (int j = 0; j < FN; ++j) {
-                const int r = wn * TNW + j * 32 + l32;
+                const int r = wn * TNW + j * MF + lrow;
                 wop[j] = *reinterpret_cast<const bf16x8*>(sW + swz(r, c) * 16);
             }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], wop[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j) {
+                    if constexpr (MF == 32)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], wop[j], acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], wop[j], acc[i][j], 0, 0, 0);
+                }
         }
     };
 
@@ -184,16 +216,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
         }
     }
 
+    if (FLAGS & EPI_RMS_PARTS) {
+        for (int r = tid; r < BM; r += NT) rsum[r] = 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PQ; ++i) {
+            const int idx = tid + NT * i, r = idx / qpr;
+            if (r < BM) atomicAdd(&rsum[r], (pss[i].x + pss[i].y) + (pss[i].z + pss[i].w));
+        }
+        __syncthreads();
+        for (int r = tid; r < BM; r += NT) rs[r] = rsqrtf(rsum[r] / (float)g.K + g.eps);
+    }
     if (FLAGS & EPI_RMS) {
         if (wn == 0) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
-                const float s2 = ss[i] + __shfl_xor(ss[i], 32, 64);
-                if (gq == 0) rs[wm * TMW + i * 32 + l32] = rsqrtf(s2 / (float)g.K + g.eps);
+                float s2 = ss[i];
+#pragma unroll
+                for (int x = MF; x < 64; x <<= 1) s2 += __shfl_xor(s2, x, 64);  // lanes sharing the row
+                if (lgrp == 0) rs[wm * TMW + i * MF + lrow] = rsqrtf(s2 / (float)g.K + g.eps);
             }
         }
     }
+    // the stage buffers are reused below (row squares): every wave is past its last LDS read
     if (FLAGS & (EPI_RMS | EPI_RMS_PARTS | EPI_ROWSS)) __syncthreads();
+    float* sq = reinterpret_cast<float*>(smem);
+    static_assert(!(FLAGS & EPI_ROWSS) || BM * (BN + 1) * 4 <= 2 * STAGE, "row squares fit the stage buffers");
 
     TC* C = (TC*)g.C[seg];
 #pragma unroll
@@ -201,10 +249,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                // 32x32 accumulator layout: column lane%32, row 8*(e/4) + 4*(lane/32) + e%4
-                const int r = wm * TMW + i * 32 + 8 * (e >> 2) + 4 * gq + (e & 3);
-                const int col = n0 + wn * TNW + j * 32 + l32;
+            for (int e = 0; e < AE; ++e) {
+                // accumulator layouts: 32x32 -> column lane%32, row 8*(e/4) + 4*(lane/32) + e%4;
+                //                      16x16 -> column lane%16, row 4*(lane/16) + e
+                const int r = wm * TMW + i * MF + (MF == 32 ? 8 * (e >> 2) + 4 * gq + (e & 3) : 4 * lgrp + e);
+                const int col = n0 + wn * TNW + j * MF + lrow;
                 const int64_t row = m0 + r;
                 if (row >= g.M) continue;
                 float v = acc[i][j][e];
@@ -215,24 +264,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
                 C[row * g.ldc + (col % g.seg_n)] = out;
                 if (FLAGS & EPI_COPY) ((bf16*)g.C2)[row * g.ldc + (col % g.seg_n)] = (bf16)v;
                 if (FLAGS & EPI_ROWSS) {
+                    // squares go to LDS (the free stage buffers) as [BM][BN+1], summed per row below
                     const float sv = to_f32(out);
-                    atomicAdd(&rsum[r], sv * sv);
+                    sq[r * (BN + 1) + (col - n0)] = sv * sv;
                 }
             }
     if (FLAGS & EPI_ROWSS) {
         static_assert(!(FLAGS & EPI_ROWSS) || BN == kRowSSTile, "row partial sums assume the fixed tile width");
         __syncthreads();
         for (int r = tid; r < BM; r += NT) {
+            float acc_r = 0.f;
+#pragma unroll 8
+            for (int c = 0; c < BN; ++c) acc_r += sq[r * (BN + 1) + c];
             const int64_t row = m0 + r;
-            if (row < g.M) g.rss_out[(int64_t)blockIdx.x * g.M + row] = rsum[r];
+            if (row < g.M) g.rss_out[row * (g.N / BN) + blockIdx.x] = acc_r;
         }
     }
 }
 
-template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D>
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32>
 static hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
     dim3 grid((uint32_t)(g.N / BN), (uint32_t)((g.M + BM - 1) / BM));
-    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D>), grid, dim3(64 * WM * WN), 0, s, g);
+    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF>), grid, dim3(64 * WM * WN), 0, s, g);
     return hipGetLastError();
 }
 
@@ -274,16 +327,19 @@ bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K) {
 template <int D>
 static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     const bool big = g.M >= 4096;
+    // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
+    // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave)
+    // keep all CUs busy; the up-front projection over N*B rows uses 128x128.
     switch (kind) {
         case GemmKind::QKV:
-            return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D>(g, s)
-                       : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D>(g, s);
+            return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D, 32>(g, s)
+                       : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
-            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D>(g, s);
-        case GemmKind::W1: return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 128, 2, 2, D>(g, s);
+            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
+        case GemmKind::W1: return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
-            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D>(g, s);
-        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D>(g, s);
+            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
+        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
     }
     return hipErrorInvalidValue;
 }

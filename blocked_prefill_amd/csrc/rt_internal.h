@@ -58,9 +58,9 @@ struct GemmArgs {
     float eps;
     int64_t M;
     int32_t N, K;
-    const float* rss_in;  // [n_parts][M] (EPI_RMS_PARTS)
+    const float* rss_in;  // [M][n_parts] (EPI_RMS_PARTS), n_parts % 4 == 0, <= 64
     int32_t n_parts;
-    float* rss_out;       // [N / tile width][M] (EPI_ROWSS)
+    float* rss_out;       // [M][N / tile width] (EPI_ROWSS)
     void* C2;             // [M][ldc] bf16 (EPI_COPY)
 };
 // Column-tile width of the GEMMs whose epilogue writes row partial sums
