@@ -43,7 +43,8 @@ rt_status check_attn(const rt_attn_desc* d) {
     if (d->dtype != RT_F32 && d->dtype != RT_BF16) return fail(RT_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
     if (d->head_dim != 32 && d->head_dim != 64 && d->head_dim != 128)
         return fail(RT_ERR_UNSUPPORTED, "head_dim %d not supported (32, 64 or 128)", d->head_dim);
-    if (!std::isfinite(d->softmax_scale)) return fail(RT_ERR_INVALID_ARG, "softmax_scale must be finite");
+    if (!std::isfinite(d->softmax_scale) || d->softmax_scale < 0.f)
+        return fail(RT_ERR_INVALID_ARG, "softmax_scale must be finite and >= 0");
     const double elems = (double)d->batch * d->seq_len * d->n_heads * d->head_dim;
     if (elems > 4.0e12) return fail(RT_ERR_UNSUPPORTED, "tensor too large");
     return RT_OK;

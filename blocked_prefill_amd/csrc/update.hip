@@ -201,33 +201,38 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
                 const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&Ks[(c32 + krow) * KSTR + 16 * i + 8 * g]);
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[i], s, 0, 0, 0);
             }
+            // running maximum on the raw scores (softmax_scale >= 0, so the
+            // scaled maximum is sigma2 times it); the reference point m_run only
+            // moves when some query's maximum exceeds it by more than 8 (base 2),
+            // so the O^T rescale is skipped by the whole wave most of the time.
             float mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[e] *= sigma2;
-                mx = fmaxf(mx, s[e]);
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sigma2;
+            const bool move = !(mx <= m_run + 8.0f);  // also true while m_run is -inf
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                const float m_new = move ? fmaxf(m_run, mx) : m_run;
+                const float alpha = fast_exp2(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    o0[e] *= alpha;
+                    o1[e] *= alpha;
+                }
+                m_run = m_new;
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fast_exp2(m_run - m_new);
             float ps = 0.f;
             bf16x8 p0, p1;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pa = fast_exp2(s[e] - m_new);
-                const float pb = fast_exp2(s[e + 8] - m_new);
+                const float pa = fast_exp2(__builtin_fmaf(s[e], sigma2, -m_run));
+                const float pb = fast_exp2(__builtin_fmaf(s[e + 8], sigma2, -m_run));
                 ps += pa + pb;
                 p0[e] = (bf16)pa;
                 p1[e] = (bf16)pb;
             }
             ps += __shfl_xor(ps, 32, 64);
-            l_run = l_run * alpha + ps;
-            m_run = m_new;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                o0[e] *= alpha;
-                o1[e] *= alpha;
-            }
+            l_run += ps;
             const bf16* v_lo = &Vt[ql * VSTR + c32 + 8 * g];
             const bf16* v_hi = &Vt[(32 + ql) * VSTR + c32 + 8 * g];
             o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_lo), p0, o0, 0, 0, 0);

@@ -60,8 +60,8 @@ typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
 /* flags of rt_layer_desc */
 #define RT_FLAG_DEBUG_SYNC 1u   /* synchronise and check after every launch (slow; for debugging) */
 
-/* Attention shape. softmax_scale multiplies every score <k, q> (the pages'
- * operator has none, i.e. 1.0; workloads use 1/sqrt(head_dim)). */
+/* Attention shape. softmax_scale (finite, >= 0) multiplies every score <k, q>
+ * (the pages' operator has none, i.e. 1.0; workloads use 1/sqrt(head_dim)). */
 typedef struct {
     int32_t batch, seq_len, n_heads, head_dim;
     rt_dtype dtype;

@@ -75,7 +75,7 @@ FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fa
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(seq_len=-3), 1), (dict(head_dim=48), 2), (dict(head_dim=256), 2),
-    (dict(dtype=7), 1), (dict(softmax_scale=float("inf")), 1),
+    (dict(dtype=7), 1), (dict(softmax_scale=float("inf")), 1), (dict(softmax_scale=-0.5), 1),
 ])
 def test_update_rejects_bad_descriptors(lib, kw, status):
     with pytest.raises(rt.RtError) as e:
