@@ -8,8 +8,9 @@ update + finalize, output projection, MLP, persistent K/V projection).
 
 Prints one JSON line. value = tokens/s of the stack (B*N tokens per step).
 roofline = the blocked-update kernel (the method's core, HBM-bound): its
-algorithmic bytes per launch over its average launch duration, timed with HIP
-events around each launch of one layer's update sequence on the launch stream.
+algorithmic bytes per launch over its average launch duration; that average
+is one layer's 2047 update launches captured as a HIP graph and replayed,
+timed with HIP events on the launch stream around the replays.
 cpu_baseline = the CPU oracle (naive schedule, fp64) on a bounded sample.
 """
 import argparse
@@ -53,6 +54,97 @@ def update_flops(t, n, p, dh):
     return 4 * dh * b * nq * p + 4 * dh * p  # block scores + PV, plus the ephemeral pair
 
 
+def measured_traffic():
+    """HBM bytes per update launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    or None when the update kernel's source has changed since those counters were taken."""
+    import hashlib
+    prof = os.path.join(ROOT, "profiles", "update_kernel_hbm_traffic_stack6_d1024_b512_n2048.txt")
+    src = os.path.join(ROOT, "blocked_prefill_amd", "csrc", "update.hip")
+    try:
+        kv = dict(ln.split("=", 1) for ln in open(prof) if "=" in ln and not ln.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["source_sha256"]:
+            return None
+        return int(kv["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True):
+    """Replay one layer's fused update steps t = 1..N-1 on the workspace's q, k', v' and state
+    (offsets as laid out by the library: q, k', v', m, l, o first). With timing_torch, each
+    launch is bracketed by HIP events on the launch stream; returns per-launch ms."""
+    import numpy as np
+    import torch
+    base = ws.data_ptr()
+    es, al = 2, lambda v: (v + 255) // 256 * 256
+    off_q = 0
+    off_ke = off_q + al(N * B * D * es)
+    off_ve = off_ke + al(N * B * D * es)
+    off_m = off_ve + al(N * B * D * es)
+    off_l = off_m + al(N * B * H * 4)
+    off_o = off_l + al(N * B * H * 4)
+    a_next = torch.empty((B, D), dtype=torch.bfloat16, device=k_cache.device)
+    timed = timing_torch is not None
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)] if timed else None
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)] if timed else None
+    if sync:
+        torch.cuda.synchronize()
+    for t in range(1, N):
+        if timed:
+            starts[t - 1].record(stream)
+        rt.rt_update_finalize_step(attn, t, base + off_q, base + off_ke, base + off_ve, k_cache, v_cache,
+                                   base + off_m, base + off_l, base + off_o, a_next, stream)
+        if timed:
+            ends[t - 1].record(stream)
+    if sync:
+        torch.cuda.synchronize()
+    if not timed:
+        return None
+    return np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)])  # ms
+
+
+def sweep(args):
+    """Single RT layer (B=512, d=1024, 16x64 heads, MLP 4096, bf16) for N = 256..2048:
+    mean of 5 graph replays after 3 warm-ups each, and the log-log slope of latency in N."""
+    import numpy as np
+    import torch
+
+    import blocked_prefill_amd as rt
+    import rt_inputs
+    rt.load()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for n in (256, 512, 1024, 2048):
+        wl = rt_inputs.Workload(f"sweep_n{n}", 512, n, 1024, 16, 64, 4096, 1, "bf16", 1003)
+        x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
+        w = rt_inputs.layer_weights(wl, 0)
+        w = {k: torch.from_numpy(w[k]).to(torch.bfloat16).to(dev) for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+        attn = rt.AttnDesc(batch=512, seq_len=n, n_heads=16, head_dim=64, dtype=rt.RT_BF16, softmax_scale=0.125)
+        desc = rt.LayerDesc(attn=attn, d_model=1024, d_ff=4096, rms_eps=1e-6, residual_scale=1.0, flags=0)
+        ws = torch.empty(rt.rt_layer_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        z, kc, vc = (torch.empty((n, 512, 1024), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        plan = rt.rt_layer_plan_create(desc, w, x, z, kc, vc, ws)
+        for _ in range(3):
+            plan.launch(stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            plan.launch(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[n] = e0.elapsed_time(e1) / 5
+        log(f"sweep N={n}: {out[n]:.2f} ms per layer")
+        plan.destroy()
+        del x, w, ws, z, kc, vc
+    ns = np.array(sorted(out))
+    slope = float(np.polyfit(np.log(ns), np.log([out[n] for n in ns]), 1)[0])
+    print(json.dumps({"sweep": "single RT layer, bf16, B=512, d=1024, 16x64 heads, MLP 4096",
+                      "ms_per_layer": {str(n): round(out[n], 3) for n in ns}, "loglog_slope": round(slope, 3)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -62,6 +154,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for hardware-counter passes: one layer forward, then its update "
+                         "sequence, then a plain 1 GiB device copy (the calibration kernel)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="single-layer latency at B=512, d=1024 for N = 256..2048 (log-log slope)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -80,6 +177,8 @@ def main():
         build.build()
     rt.load()
 
+    if args.sweep:
+        return sweep(args)
     wl = rt_inputs.WORKLOADS[args.workload]
     N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
     scale = 1.0 / math.sqrt(dh)
@@ -103,6 +202,17 @@ def main():
     zs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     ks = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     vs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+
+    if args.counters:
+        # one layer forward (fills q, k', v' and the KV cache), then its update sequence, then the copy
+        rt.rt_layer_forward(desc, weights[0], x, zs[0], ks[0], vs[0], ws, stream=stream)
+        update_sequence(rt, attn, ws, ks[0], vs[0], N, B, H, D, stream, None)
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("counters run done: layer forward, 2047 update launches, 1 GiB copy")
+        return
 
     t0 = time.time()
     plans = []
@@ -143,32 +253,33 @@ def main():
     if not args.no_kernel_timing:
         # the last layer's q, k', v' and state are in the workspace, its caches in ks/vs:
         # replay its update sequence (t = 1..N-1), one event pair per launch
-        base = ws.data_ptr()
-        es, al = 2, lambda v: (v + 255) // 256 * 256
-        off_q = 0
-        off_ke = off_q + al(N * B * D * es)
-        off_ve = off_ke + al(N * B * D * es)
-        off_m = off_ve + al(N * B * D * es)
-        off_l = off_m + al(N * B * H * 4)
-        off_o = off_l + al(N * B * H * 4)
-        a_next = torch.empty((B, D), dtype=torch.bfloat16, device=dev)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)]
+        durs = update_sequence(rt, attn, ws, ks[-1], vs[-1], N, B, H, D, stream, torch)
+        # the roofline's average launch duration: the same 2047 launches captured as one HIP
+        # graph and replayed back to back, two events on the launch stream around the replays
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                update_sequence(rt, attn, ws, ks[-1], vs[-1], N, B, H, D, cap, None, sync=False)
         torch.cuda.synchronize()
-        for t in range(1, N):
-            starts[t - 1].record(stream)
-            rt.rt_update_finalize_step(attn, t, base + off_q, base + off_ke, base + off_ve, ks[-1], vs[-1],
-                                       base + off_m, base + off_l, base + off_o, a_next, stream)
-            ends[t - 1].record(stream)
+        g.replay()
         torch.cuda.synchronize()
-        durs = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])  # ms
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        r0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        graph_avg_s = r0.elapsed_time(r1) / 1e3 / (reps * (N - 1))
+        del g
         P = B * H
         byts = np.array([update_bytes(t, N, P, dh, 2) for t in range(1, N)], dtype=np.float64)
         flops = np.array([update_flops(t, N, P, dh) for t in range(1, N)], dtype=np.float64)
-        avg_s = durs.mean() / 1e3
+        avg_s = graph_avg_s
         achieved = byts.mean() / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                     "kernel": "update_simt_kernel<bf16,64> (fused blocked update + finalize)",
                     "launches": N - 1, "avg_launch_us": round(avg_s * 1e6, 2),
                     "alg_bytes_per_launch": int(byts.mean())}
@@ -181,7 +292,8 @@ def main():
             lv[2] += flops[t - 1]
             lv[3] += 1
         update_info = {
-            "update_ms_per_layer": round(float(durs.sum()), 3),
+            "update_ms_per_layer": round(avg_s * (N - 1) * 1e3, 3),
+            "per_level_timing": "HIP events around each launch (adds the event records' overhead)",
             "update_alg_GB_per_layer": round(float(byts.sum()) / 1e9, 3),
             "per_level": {str(b): {"steps": v[3], "us_per_step": round(v[0] / v[3] * 1e3, 2),
                                    "GB_s": round(v[1] / (v[0] / 1e3) / 1e9, 1),
@@ -189,7 +301,7 @@ def main():
                           for b, v in sorted(levels.items())},
         }
         log(f"update kernel: {achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of HBM peak), "
-            f"{durs.sum():.2f} ms per layer")
+            f"{avg_s * (N - 1) * 1e3:.2f} ms per layer")
 
     cpu = None
     if not args.no_cpu:
