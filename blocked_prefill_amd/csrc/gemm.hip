@@ -238,12 +238,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
             }
         }
     }
-    // the stage buffers are reused below (row squares): every wave is past its last LDS read
-    if (FLAGS & (EPI_RMS | EPI_RMS_PARTS | EPI_ROWSS)) __syncthreads();
-    float* sq = reinterpret_cast<float*>(smem);
-    static_assert(!(FLAGS & EPI_ROWSS) || BM * (BN + 1) * 4 <= 2 * STAGE, "row squares fit the stage buffers");
-
+    // Epilogue. The fp32 tile goes through LDS (the free stage buffers) so that
+    // each thread then owns runs of 8 consecutive columns of one row: 16-byte
+    // stores and residual loads, and each 32-column group's sum of squares is a
+    // 4-lane shuffle.
+    constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
+    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes)
+    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : BM / 2;
+    static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
+    constexpr int CPRW = BN / 8;               // 8-column runs per row
+    constexpr int RUNS = PR * CPRW / NT;       // runs per thread per pass
+    static_assert((PR * CPRW) % NT == 0 && NT % CPRW == 0, "runs divide evenly");
+    static_assert(!(FLAGS & EPI_ROWSS) || (BN % kRowSSTile == 0 && CPRW >= 4), "32-column groups");
+    float* tl = reinterpret_cast<float*>(smem);
     TC* C = (TC*)g.C[seg];
+#pragma unroll
+    for (int pass = 0; pass < BM / PR; ++pass) {
+    __syncthreads();  // the stage buffers are free (last reads done; rs ready; previous pass consumed)
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -253,32 +264,74 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
                 // accumulator layouts: 32x32 -> column lane%32, row 8*(e/4) + 4*(lane/32) + e%4;
                 //                      16x16 -> column lane%16, row 4*(lane/16) + e
                 const int r = wm * TMW + i * MF + (MF == 32 ? 8 * (e >> 2) + 4 * gq + (e & 3) : 4 * lgrp + e);
-                const int col = n0 + wn * TNW + j * MF + lrow;
-                const int64_t row = m0 + r;
-                if (row >= g.M) continue;
-                float v = acc[i][j][e];
-                if (FLAGS & (EPI_RMS | EPI_RMS_PARTS)) v *= rs[r];
-                if (FLAGS & EPI_GELU) v = gelu_erf(v);
-                if (FLAGS & EPI_RESID) v = to_f32(((const TR*)g.R)[row * g.ldr + col]) + g.rscale * v;
-                const TC out = from_f32<TC>(v);
-                C[row * g.ldc + (col % g.seg_n)] = out;
-                if (FLAGS & EPI_COPY) ((bf16*)g.C2)[row * g.ldc + (col % g.seg_n)] = (bf16)v;
-                if (FLAGS & EPI_ROWSS) {
-                    // squares go to LDS (the free stage buffers) as [BM][BN+1], summed per row below
-                    const float sv = to_f32(out);
-                    sq[r * (BN + 1) + (col - n0)] = sv * sv;
-                }
+                const int c = wn * TNW + j * MF + lrow;
+                if (r >= pass * PR && r < (pass + 1) * PR) tl[(r - pass * PR) * LDT + c] = acc[i][j][e];
             }
-    if (FLAGS & EPI_ROWSS) {
-        static_assert(!(FLAGS & EPI_ROWSS) || BN == kRowSSTile, "row partial sums assume the fixed tile width");
-        __syncthreads();
-        for (int r = tid; r < BM; r += NT) {
-            float acc_r = 0.f;
-#pragma unroll 8
-            for (int c = 0; c < BN; ++c) acc_r += sq[r * (BN + 1) + c];
-            const int64_t row = m0 + r;
-            if (row < g.M) g.rss_out[row * (g.N / BN) + blockIdx.x] = acc_r;
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < RUNS; ++it) {
+        const int x = tid + NT * it;
+        const int rl = x / CPRW, c0 = (x % CPRW) * 8;
+        const int r = pass * PR + rl;
+        const int64_t row = m0 + r;
+        const bool ok = row < g.M;
+        const int col = n0 + c0;
+        float v[8];
+        {
+            const float4 p0 = *reinterpret_cast<const float4*>(&tl[rl * LDT + c0]);
+            const float4 p1 = *reinterpret_cast<const float4*>(&tl[rl * LDT + c0 + 4]);
+            v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+            v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
         }
+        if (FLAGS & (EPI_RMS | EPI_RMS_PARTS)) {
+            const float sc = rs[r];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= sc;
+        }
+        if (FLAGS & EPI_GELU) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
+        }
+        if ((FLAGS & EPI_RESID) && ok) {
+            float res[8];
+            load8((const TR*)g.R + row * g.ldr + col, res);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = res[e] + g.rscale * v[e];
+        }
+        float stored[8];
+        if (ok) {
+            TC* dst = C + row * g.ldc + (col % g.seg_n);
+            if constexpr (sizeof(TC) == 2) {
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[e] = (bf16)v[e];
+                    stored[e] = (float)o[e];
+                }
+                *reinterpret_cast<bf16x8*>(dst) = o;
+            } else {
+                store8((float*)dst, v);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) stored[e] = v[e];
+            }
+            if (FLAGS & EPI_COPY) {
+                bf16x8 o;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
+                *reinterpret_cast<bf16x8*>((bf16*)g.C2 + row * g.ldc + (col % g.seg_n)) = o;
+            }
+        }
+        if (FLAGS & EPI_ROWSS) {
+            // sum of squares of the stored values over this row's 32-column group:
+            // the group's 4 runs sit in 4 consecutive lanes
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq += ok ? stored[e] * stored[e] : 0.f;
+            sq += __shfl_xor(sq, 1, 64);
+            sq += __shfl_xor(sq, 2, 64);
+            if (ok && (x % 4) == 0) g.rss_out[row * (g.N / kRowSSTile) + col / kRowSSTile] = sq;
+        }
+    }
     }
 }
 
