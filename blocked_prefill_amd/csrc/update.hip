@@ -97,6 +97,13 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
     }
 }
 
+// Workgroup barrier ordering LDS accesses only: global loads stay in flight across it.
+__device__ __forceinline__ void lds_fence_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // MFMA update for blocks of b >= 32 pairs, head_dim 64, bf16 (gfx950).
 //
 // A workgroup of WAVES waves takes one (batch*head pair p, tile of 32*WAVES
@@ -169,28 +176,53 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     const int krow = (ql & ~12) | ((ql & 4) << 1) | ((ql & 8) >> 1);
     const float sigma2 = a.sigma2;
 
-    for (int kt0 = 0; kt0 < a.nkv; kt0 += KT) {
+    // K/V tiles are fetched into registers one tile ahead: tile i+1's loads are
+    // in flight while tile i is multiplied (LDS-only barriers keep them in flight).
+    constexpr int KCH = KT * 8 / NT;        // 16-byte K chunks per thread per tile
+    constexpr int VCH = (KT / 2) * 8 / NT;  // V row-pair chunks per thread per tile
+    static_assert(KCH >= 1 && VCH >= 1 && (KT * 8) % NT == 0 && ((KT / 2) * 8) % NT == 0, "tile staging");
+    bf16x8 kreg[KCH], vreg[VCH][2];
+    auto fetch = [&](int kt0) {
         const int rows = (a.nkv - kt0) < KT ? (a.nkv - kt0) : KT;  // 32 or 64
-        __syncthreads();
-        for (int c = tid; c < rows * 8; c += NT) {
-            const int r = c >> 3, ch = (c & 7) * 8;
-            *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + ch]) =
-                *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
-        }
-        for (int c = tid; c < (rows / 2) * 8; c += NT) {
-            const int r0 = (c >> 3) * 2, ch = (c & 7) * 8;
-            const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch);
-            const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-                bf16x2 w;
-                w[0] = v0[i];
-                w[1] = v1[i];
-                *reinterpret_cast<bf16x2*>(&Vt[(ch + i) * VSTR + r0]) = w;
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + NT * i, r = c >> 3, ch = (c & 7) * 8;
+            if (r < rows) kreg[i] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
+            if (r0 < rows) {
+                vreg[i][0] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch);
+                vreg[i][1] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch);
             }
         }
-        __syncthreads();
+    };
+    fetch(0);
+    for (int kt0 = 0; kt0 < a.nkv; kt0 += KT) {
+        const int rows = (a.nkv - kt0) < KT ? (a.nkv - kt0) : KT;  // 32 or 64
+        lds_fence_barrier();  // the previous tile's LDS reads are done
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + NT * i, r = c >> 3, ch = (c & 7) * 8;
+            if (r < rows) *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + ch]) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VCH; ++i) {
+            const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
+            if (r0 < rows) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+                    bf16x2 w;
+                    w[0] = vreg[i][0][e];
+                    w[1] = vreg[i][1][e];
+                    *reinterpret_cast<bf16x2*>(&Vt[(ch + e) * VSTR + r0]) = w;
+                }
+            }
+        }
+        lds_fence_barrier();  // this tile is in LDS
+        if (kt0 + KT < a.nkv) fetch(kt0 + KT);
         if (!wave_active) continue;
         for (int c32 = 0; c32 < rows; c32 += 32) {
             f32x16 s;
