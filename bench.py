@@ -104,10 +104,67 @@ def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_t
     return np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)])  # ms
 
 
+SWEEP_VARIANTS = {"rt_blocked": 0, "rt_naive": 2, "transformer": 4}  # rt_layer_desc flags
+
+
+def _sweep_layer(rt, n, flags, dev, stream, warm, reps):
+    """Mean ms of `reps` graph replays of one layer (B=512, d=1024, 16x64 heads,
+    MLP 4096, bf16) after `warm` replays."""
+    import torch
+    import rt_inputs
+    wl = rt_inputs.Workload(f"sweep_n{n}", 512, n, 1024, 16, 64, 4096, 1, "bf16", 1003)
+    x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
+    w = rt_inputs.layer_weights(wl, 0)
+    w = {k: torch.from_numpy(w[k]).to(torch.bfloat16).to(dev) for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    attn = rt.AttnDesc(batch=512, seq_len=n, n_heads=16, head_dim=64, dtype=rt.RT_BF16, softmax_scale=0.125)
+    desc = rt.LayerDesc(attn=attn, d_model=1024, d_ff=4096, rms_eps=1e-6, residual_scale=1.0, flags=flags)
+    ws = torch.empty(rt.rt_layer_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    z, kc, vc = (torch.empty((n, 512, 1024), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    plan = rt.rt_layer_plan_create(desc, w, x, z, kc, vc, ws)
+    for _ in range(warm):
+        plan.launch(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        plan.launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan.destroy()
+    return e0.elapsed_time(e1) / reps
+
+
 def sweep(args):
-    """Single RT layer (B=512, d=1024, 16x64 heads, MLP 4096, bf16) for N = 256..2048:
-    mean of 5 graph replays after 3 warm-ups each, and the log-log slope of latency in N."""
+    """Single-layer forward latency against N = 256..2048 at B=512, d=1024 for the
+    RT layer under the blocked and the naive schedule and for the standard
+    Transformer layer (the three curves of the translated paper's Figure 4), and
+    each curve's log-log slope."""
     import numpy as np
+    import torch
+
+    import blocked_prefill_amd as rt
+    rt.load()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    ns = (256, 512, 1024, 2048)
+    res = {}
+    for name, flags in SWEEP_VARIANTS.items():
+        res[name] = {}
+        for n in ns:
+            slow = name == "rt_naive" and n >= 1024
+            res[name][n] = _sweep_layer(rt, n, flags, dev, stream, 1 if slow else 3, 2 if slow else 5)
+            log(f"sweep {name} N={n}: {res[name][n]:.2f} ms per layer")
+    out = {"sweep": "single layer forward, bf16, B=512, d=1024, 16x64 heads, MLP 4096",
+           "ms_per_layer": {k: {str(n): round(v[n], 3) for n in ns} for k, v in res.items()},
+           "loglog_slope": {k: round(float(np.polyfit(np.log(ns), np.log([v[n] for n in ns]), 1)[0]), 3)
+                            for k, v in res.items()}}
+    print(json.dumps(out))
+
+
+def decode(args):
+    """One decode step (a new position per sequence against the persistent KV
+    cache) of the B=512, d=1024 layer after a 2048-position prefill: mean of
+    20 steps (the same position re-decoded), and the cache-read roofline."""
     import torch
 
     import blocked_prefill_amd as rt
@@ -115,34 +172,42 @@ def sweep(args):
     rt.load()
     dev = torch.device("cuda", 0)
     stream = torch.cuda.current_stream()
-    out = {}
-    for n in (256, 512, 1024, 2048):
-        wl = rt_inputs.Workload(f"sweep_n{n}", 512, n, 1024, 16, 64, 4096, 1, "bf16", 1003)
-        x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
-        w = rt_inputs.layer_weights(wl, 0)
-        w = {k: torch.from_numpy(w[k]).to(torch.bfloat16).to(dev) for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
-        attn = rt.AttnDesc(batch=512, seq_len=n, n_heads=16, head_dim=64, dtype=rt.RT_BF16, softmax_scale=0.125)
-        desc = rt.LayerDesc(attn=attn, d_model=1024, d_ff=4096, rms_eps=1e-6, residual_scale=1.0, flags=0)
-        ws = torch.empty(rt.rt_layer_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-        z, kc, vc = (torch.empty((n, 512, 1024), dtype=torch.bfloat16, device=dev) for _ in range(3))
-        plan = rt.rt_layer_plan_create(desc, w, x, z, kc, vc, ws)
-        for _ in range(3):
-            plan.launch(stream)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(5):
-            plan.launch(stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        out[n] = e0.elapsed_time(e1) / 5
-        log(f"sweep N={n}: {out[n]:.2f} ms per layer")
-        plan.destroy()
-        del x, w, ws, z, kc, vc
-    ns = np.array(sorted(out))
-    slope = float(np.polyfit(np.log(ns), np.log([out[n] for n in ns]), 1)[0])
-    print(json.dumps({"sweep": "single RT layer, bf16, B=512, d=1024, 16x64 heads, MLP 4096",
-                      "ms_per_layer": {str(n): round(out[n], 3) for n in ns}, "loglog_slope": round(slope, 3)}))
+    B, D, H, dh, F, n_past = 512, 1024, 16, 64, 4096, 2048
+    wl = rt_inputs.Workload("decode_b512_n2048", B, n_past, D, H, dh, F, 1, "bf16", 1003)
+    w = rt_inputs.layer_weights(wl, 0)
+    w = {k: torch.from_numpy(w[k]).to(torch.bfloat16).to(dev) for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    attn = rt.AttnDesc(batch=B, seq_len=n_past + 1, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=0.125)
+    desc = rt.LayerDesc(attn=attn, d_model=D, d_ff=F, rms_eps=1e-6, residual_scale=1.0, flags=0)
+    pre = rt.LayerDesc(attn=rt.AttnDesc(batch=B, seq_len=n_past, n_heads=H, head_dim=dh, dtype=rt.RT_BF16,
+                                        softmax_scale=0.125), d_model=D, d_ff=F, rms_eps=1e-6, residual_scale=1.0,
+                       flags=0)
+    x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
+    kc, vc = (torch.empty((n_past + 1, B, D), dtype=torch.bfloat16, device=dev) for _ in range(2))
+    z = torch.empty((n_past, B, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rt.rt_layer_workspace_bytes(pre), dtype=torch.uint8, device=dev)
+    rt.rt_layer_forward(pre, w, x, z, kc[:n_past], vc[:n_past], ws, stream=stream)
+    torch.cuda.synchronize()
+    del ws
+    x_new = x[-1].clone()
+    z_new = torch.empty((B, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rt.rt_layer_decode_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        rt.rt_layer_decode_step(desc, w, n_past, x_new, z_new, kc, vc, ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        rt.rt_layer_decode_step(desc, w, n_past, x_new, z_new, kc, vc, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    cache_bytes = 2 * n_past * B * D * 2
+    weight_bytes = (4 * D * D + 2 * D * F) * 2
+    floor_ms = (cache_bytes + weight_bytes) / (HBM_PEAK_GBS * 1e9) * 1e3
+    print(json.dumps({"decode": "one RT layer, bf16, B=512, d=1024, 16x64 heads, MLP 4096, after 2048 positions",
+                      "ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms * 1e-3), 1),
+                      "hbm_floor_ms": round(floor_ms, 4), "frac_of_floor": round(floor_ms / ms, 4)}))
 
 
 def main():
@@ -158,7 +223,10 @@ def main():
                     help="short run for hardware-counter passes: one layer forward, then its update "
                          "sequence, then a plain 1 GiB device copy (the calibration kernel)")
     ap.add_argument("--sweep", action="store_true",
-                    help="single-layer latency at B=512, d=1024 for N = 256..2048 (log-log slope)")
+                    help="single-layer latency at B=512, d=1024 for N = 256..2048: RT blocked, RT naive, "
+                         "Transformer (log-log slopes)")
+    ap.add_argument("--decode", action="store_true",
+                    help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -179,6 +247,8 @@ def main():
 
     if args.sweep:
         return sweep(args)
+    if args.decode:
+        return decode(args)
     wl = rt_inputs.WORKLOADS[args.workload]
     N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
     scale = 1.0 / math.sqrt(dh)

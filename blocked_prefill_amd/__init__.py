@@ -14,11 +14,14 @@ __all__ = [
     "RT_F32", "RT_BF16", "RtError", "AttnDesc", "LayerDesc", "LayerWeights", "load", "library_path",
     "rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes",
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
-    "rt_last_error", "EXPORTED",
+    "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_last_error", "EXPORTED",
+    "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER",
 ]
 
 RT_F32, RT_BF16 = 0, 1
 RT_FLAG_DEBUG_SYNC = 1
+RT_FLAG_NAIVE_SCHEDULE = 2
+RT_FLAG_TRANSFORMER = 4
 _STATUS = {0: "RT_OK", 1: "RT_ERR_INVALID_ARG", 2: "RT_ERR_UNSUPPORTED", 3: "RT_ERR_WORKSPACE", 4: "RT_ERR_HIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,7 +30,7 @@ library_path = os.path.join(_HERE, "librt_prefill.so")
 # every symbol include/rt_prefill.h declares
 EXPORTED = ["rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes", "rt_layer_forward",
             "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
-            "rt_last_error"]
+            "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_last_error"]
 
 
 class RtError(RuntimeError):
@@ -71,6 +74,8 @@ def load():
             "rt_layer_plan_create": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, ctypes.POINTER(_vp)],
             "rt_layer_plan_launch": [_vp, _vp],
+            "rt_layer_decode_step": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _i32, _vp, _vp, _vp,
+                                     _vp, _vp, ctypes.c_size_t, _vp],
             "rt_schedule_step": [_i32, _i32] + [ctypes.POINTER(_i32)] * 4,
         }
         for name, args in sig.items():
@@ -79,6 +84,8 @@ def load():
             f.restype = ctypes.c_int
         L.rt_layer_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.rt_layer_workspace_bytes.restype = ctypes.c_size_t
+        L.rt_layer_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.rt_layer_decode_workspace_bytes.restype = ctypes.c_size_t
         L.rt_layer_plan_destroy.argtypes = [_vp]
         L.rt_layer_plan_destroy.restype = None
         L.rt_last_error.argtypes = []
@@ -151,6 +158,18 @@ def rt_layer_forward(desc: LayerDesc, weights, x, z, k_cache, v_cache, workspace
     W = _weights(weights)
     _check(load().rt_layer_forward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(z), _ptr(k_cache),
                                    _ptr(v_cache), _ptr(workspace), ws, _stream(stream)))
+
+
+def rt_layer_decode_workspace_bytes(desc: LayerDesc) -> int:
+    return int(load().rt_layer_decode_workspace_bytes(ctypes.byref(desc)))
+
+
+def rt_layer_decode_step(desc: LayerDesc, weights, n_past: int, x_t, z_t, k_cache, v_cache, workspace,
+                         workspace_bytes=None, stream=None):
+    ws = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    W = _weights(weights)
+    _check(load().rt_layer_decode_step(ctypes.byref(desc), ctypes.byref(W), n_past, _ptr(x_t), _ptr(z_t),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(workspace), ws, _stream(stream)))
 
 
 class Plan:

@@ -62,27 +62,49 @@ rt_status check_layer(const rt_layer_desc* d) {
     if (!std::isfinite(d->residual_scale)) return fail(RT_ERR_INVALID_ARG, "residual_scale must be finite");
     if (d->attn.dtype == RT_BF16 && (d->d_model % 128 || d->d_ff % 128))
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers need d_model and d_ff multiples of 128");
+    if ((d->flags & RT_FLAG_NAIVE_SCHEDULE) && (d->flags & RT_FLAG_TRANSFORMER))
+        return fail(RT_ERR_INVALID_ARG, "RT_FLAG_NAIVE_SCHEDULE and RT_FLAG_TRANSFORMER exclude each other");
+    if (d->flags & ~(RT_FLAG_DEBUG_SYNC | RT_FLAG_NAIVE_SCHEDULE | RT_FLAG_TRANSFORMER))
+        return fail(RT_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
     if (d->attn.dtype == RT_BF16 && d->d_model > 64 * rt::kRowSSTile)
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers support d_model up to %d", 64 * rt::kRowSSTile);
     return RT_OK;
 }
 
+// What a workspace is laid out for.
+enum class Mode {
+    Blocked,      // RT layer, blocked schedule (the default)
+    Naive,        // RT layer, naive schedule: position t's query reads pairs 1..t-1 in one pass
+    Transformer,  // standard layer: pairs from the input, every position at once
+    Decode,       // one RT (or Transformer) position against a cache
+};
+
+Mode mode_of(const rt_layer_desc* d) {
+    if (d->flags & RT_FLAG_TRANSFORMER) return Mode::Transformer;
+    if (d->flags & RT_FLAG_NAIVE_SCHEDULE) return Mode::Naive;
+    return Mode::Blocked;
+}
+
 // Workspace layout of one layer forward (byte offsets, 256-aligned).
+// Sizes below are for the blocked schedule; "rows" is B for the modes that
+// run position by position and N*B for the Transformer layer.
 struct Layout {
     size_t q, ke, ve;     // [N][B][d] dtype: queries and ephemeral pairs, formed up front
-    size_t m, l, o;       // [N][B][H], [N][B][H], [N][B][H][dh] fp32: online-softmax state
-    size_t a;             // [B][d] dtype: attention output of the current position
-    size_t h;             // [B][d] fp32: residual stream after the attention branch
-    size_t g;             // [B][F] dtype: MLP hidden activation
-    size_t hb;            // [B][d] bf16: h rounded, the MLP's first operand (bf16 layers)
-    size_t hss, zss;      // [B][d/32] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
+    size_t m, l, o;       // [N][B][H], [N][B][H], [N][B][H][dh] fp32: online-softmax state (blocked only)
+    size_t a;             // [rows][d] dtype: attention output
+    size_t h;             // [rows][d] fp32: residual stream after the attention branch
+    size_t g;             // [rows][F] dtype: MLP hidden activation
+    size_t hb;            // [rows][d] bf16: h rounded, the MLP's first operand (bf16 layers)
+    size_t hss, zss;      // [rows][d/32] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
     size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
     size_t total;
 };
 
-Layout layout_of(const rt_layer_desc* d) {
+Layout layout_of(const rt_layer_desc* d, Mode mode) {
     const size_t es = elem_bytes(d->attn.dtype);
-    const size_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, D = d->d_model, F = d->d_ff;
+    const size_t N = mode == Mode::Decode ? 1 : d->attn.seq_len;
+    const size_t B = d->attn.batch, H = d->attn.n_heads, D = d->d_model, F = d->d_ff;
+    const size_t rows = mode == Mode::Transformer ? N * B : B;
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -91,17 +113,21 @@ Layout layout_of(const rt_layer_desc* d) {
         return at;
     };
     L.q = take(N * B * D * es);
-    L.ke = take(N * B * D * es);
-    L.ve = take(N * B * D * es);
-    L.m = take(N * B * H * 4);
-    L.l = take(N * B * H * 4);
-    L.o = take(N * B * D * 4);
-    L.a = take(B * D * es);
-    L.h = take(B * D * 4);
-    L.g = take(B * F * es);
-    L.hb = take(B * D * 2);
-    L.hss = take(D / rt::kRowSSTile * B * 4 + 4);
-    L.zss = take(D / rt::kRowSSTile * B * 4 + 4);
+    if (mode != Mode::Transformer) {  // (the Transformer's pairs go straight into the caches)
+        L.ke = take(N * B * D * es);
+        L.ve = take(N * B * D * es);
+    }
+    if (mode == Mode::Blocked) {
+        L.m = take(N * B * H * 4);
+        L.l = take(N * B * H * 4);
+        L.o = take(N * B * D * 4);
+    }
+    L.a = take(rows * D * es);
+    L.h = take(rows * D * 4);
+    L.g = take(rows * F * es);
+    L.hb = take(rows * D * 2);
+    L.hss = take(D / rt::kRowSSTile * rows * 4 + 4);
+    L.zss = take(D / rt::kRowSSTile * rows * 4 + 4);
     L.wq = take(D * D * es);
     L.wk = take(D * D * es);
     L.wv = take(D * D * es);
@@ -143,101 +169,188 @@ rt_status check_layer_ptrs(const rt_layer_weights* w, const void* x, void* z, vo
     return RT_OK;
 }
 
-// Enqueue the whole layer forward on stream s (eager, or inside a capture).
-rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const void* x, void* z, void* kc,
-                        void* vc, void* ws, hipStream_t s, bool debug) {
+// The projections each RMS normalisation feeds, with the gain folded in
+// (W'[r][c] = W[r][c] g[c]) when a gain is given.
+struct Projections {
+    const void *wq, *wk, *wv, *w1;
+};
+
+rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* base, const Layout& L,
+                       Launcher& run, Projections* p) {
     using namespace rt;
     const rt_dtype dt = d->attn.dtype;
-    const size_t es = elem_bytes(dt);
-    const int32_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, dh = d->attn.head_dim;
     const int32_t D = d->d_model, F = d->d_ff;
-    const Layout L = layout_of(d);
-    char* base = (char*)ws;
-    void *q = base + L.q, *ke = base + L.ke, *ve = base + L.ve;
-    float *m = (float*)(base + L.m), *l = (float*)(base + L.l), *o = (float*)(base + L.o);
-    void *a = base + L.a, *g = base + L.g;
-    float* h = (float*)(base + L.h);
-    Launcher run{s, debug};
-
-    // gains folded into the projections that follow each RMS normalisation
-    const void *wq = w->w_q, *wk = w->w_k, *wv = w->w_v, *w1 = w->w_1;
+    hipStream_t s = run.s;
+    *p = Projections{w->w_q, w->w_k, w->w_v, w->w_1};
     if (w->g_attn) {
         RT_TRY(run.check(launch_fold_gain(dt, w->w_q, w->g_attn, base + L.wq, D, D, s), "fold g_attn"));
         RT_TRY(run.check(launch_fold_gain(dt, w->w_k, w->g_attn, base + L.wk, D, D, s), "fold g_attn"));
         RT_TRY(run.check(launch_fold_gain(dt, w->w_v, w->g_attn, base + L.wv, D, D, s), "fold g_attn"));
-        wq = base + L.wq;
-        wk = base + L.wk;
-        wv = base + L.wv;
+        p->wq = base + L.wq;
+        p->wk = base + L.wk;
+        p->wv = base + L.wv;
     }
     if (w->g_mlp) {
         RT_TRY(run.check(launch_fold_gain(dt, w->w_1, w->g_mlp, base + L.w1, F, D, s), "fold g_mlp"));
-        w1 = base + L.w1;
+        p->w1 = base + L.w1;
     }
+    return RT_OK;
+}
 
-    // every query and ephemeral pair depends only on the input: one GEMM up front
+// q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x.
+rt_status enqueue_qkv(const rt_layer_desc* d, const Projections& p, const void* x, int64_t rows, void* q, void* ke,
+                      void* ve, Launcher& run) {
+    using namespace rt;
+    const int32_t D = d->d_model;
     GemmArgs gq{};
     gq.A = x; gq.lda = D;
-    gq.W[0] = wq; gq.W[1] = wk; gq.W[2] = wv;
+    gq.W[0] = p.wq; gq.W[1] = p.wk; gq.W[2] = p.wv;
     gq.C[0] = q; gq.C[1] = ke; gq.C[2] = ve;
     gq.ldc = D; gq.seg_n = D; gq.eps = d->rms_eps;
-    gq.M = (int64_t)N * B; gq.N = 3 * D; gq.K = D;
-    RT_TRY(run.check(launch_gemm(dt, GemmKind::QKV, gq, s), "qkv projection"));
+    gq.M = rows; gq.N = 3 * D; gq.K = D;
+    return run.check(launch_gemm(d->attn.dtype, GemmKind::QKV, gq, run.s), "qkv projection");
+}
 
-    const int64_t P = (int64_t)B * H;
-    const float sigma2 = d->attn.softmax_scale * kLog2eHost;
+// Everything after the attention, for `rows` rows:
+//   h = x + rho W_o a;  z = h + rho W_2 GELU(W_1 RMS_mlp(h));
+//   and, when kt is not NULL, the persistent pair k|v = W_{k,v} RMS_attn(z).
+rt_status enqueue_tail(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, char* base,
+                       const Layout& L, int64_t rows, const void* a, const void* x, void* z, void* kt, void* vt,
+                       Launcher& run) {
+    using namespace rt;
+    const rt_dtype dt = d->attn.dtype;
+    const int32_t D = d->d_model, F = d->d_ff;
+    hipStream_t s = run.s;
+    void* g = base + L.g;
+    float* h = (float*)(base + L.h);
+    // bf16 layers: W_o also stores h rounded to bf16 (the MLP's operand) and
+    // per-row partial sums of h^2; W_2 stores partial sums of z^2 (z as stored).
+    // The next GEMM turns those sums into its RMS row scale.
+    const bool b16 = dt == RT_BF16;
+    const int32_t parts = D / kRowSSTile;
+
+    GemmArgs go{};  // h = x + rho W_o a
+    go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
+    go.R = x; go.ldr = D; go.rscale = d->residual_scale; go.M = rows; go.N = D; go.K = D;
+    if (b16) { go.C2 = base + L.hb; go.rss_out = (float*)(base + L.hss); }
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "output projection"));
+
+    GemmArgs g1{};  // g = GELU(W_1 RMS_mlp(h))
+    g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = p.w1; g1.C[0] = g;
+    g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = rows; g1.N = F; g1.K = D;
+    if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, g1, s), "mlp up"));
+
+    GemmArgs g2{};  // z = h + rho W_2 g
+    g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = z; g2.ldc = D; g2.seg_n = D;
+    g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = rows; g2.N = D; g2.K = F;
+    if (b16) g2.rss_out = (float*)(base + L.zss);
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, g2, s), "mlp down"));
+
+    if (!kt) return RT_OK;
+    GemmArgs gk{};  // persistent pair from the output z
+    gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = kt; gk.C[1] = vt;
+    gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
+    if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
+    return run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection");
+}
+
+// The standard Transformer layer: the pairs come from the input, so every
+// position is computed at once: one projection, one causal attention, and the
+// tail over all N*B rows. The pairs are written straight into the caches.
+rt_status enqueue_transformer(const rt_layer_desc* d, const rt_layer_weights* w, const void* x, void* z, void* kc,
+                              void* vc, void* ws, Launcher& run) {
+    using namespace rt;
+    const int64_t rows = (int64_t)d->attn.seq_len * d->attn.batch;
+    const Layout L = layout_of(d, Mode::Transformer);
+    char* base = (char*)ws;
+    Projections p;
+    RT_TRY(enqueue_fold(d, w, base, L, run, &p));
+    RT_TRY(enqueue_qkv(d, p, x, rows, base + L.q, kc, vc, run));
     UpdateArgs u{};
-    u.q = q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve;
-    u.m = m; u.l = l; u.o = o; u.a_out = a; u.P = P; u.sigma2 = sigma2;
+    u.q = base + L.q; u.k = kc; u.v = vc; u.a_out = base + L.a;
+    u.P = (int64_t)d->attn.batch * d->attn.n_heads; u.nq = d->attn.seq_len;
+    u.sigma2 = d->attn.softmax_scale * kLog2eHost; u.init = 1;
+    RT_TRY(run.check(launch_causal_attention(d->attn.dtype, d->attn.head_dim, u, run.s), "causal attention"));
+    return enqueue_tail(d, w, p, base, L, rows, base + L.a, x, z, nullptr, nullptr, run);
+}
+
+// Enqueue the whole layer forward on stream s (eager, or inside a capture).
+rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const void* x, void* z, void* kc,
+                        void* vc, void* ws, hipStream_t s, bool debug) {
+    using namespace rt;
+    Launcher run{s, debug};
+    const Mode mode = mode_of(d);
+    if (mode == Mode::Transformer) return enqueue_transformer(d, w, x, z, kc, vc, ws, run);
+
+    const rt_dtype dt = d->attn.dtype;
+    const size_t es = elem_bytes(dt);
+    const int32_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, dh = d->attn.head_dim;
+    const Layout L = layout_of(d, mode);
+    char* base = (char*)ws;
+    void *q = base + L.q, *ke = base + L.ke, *ve = base + L.ve, *a = base + L.a;
+    Projections p;
+    RT_TRY(enqueue_fold(d, w, base, L, run, &p));
+
+    // every query and ephemeral pair depends only on the input: one GEMM up front
+    RT_TRY(enqueue_qkv(d, p, x, (int64_t)N * B, q, ke, ve, run));
+
+    UpdateArgs u{};
+    u.q = q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = a;
+    if (mode == Mode::Blocked) {
+        u.m = (float*)(base + L.m); u.l = (float*)(base + L.l); u.o = (float*)(base + L.o);
+    }
+    u.P = (int64_t)B * H; u.sigma2 = d->attn.softmax_scale * kLog2eHost;
     // position 1: empty state, a_1 is its own ephemeral value
     u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
     RT_TRY(run.check(launch_update(dt, dh, u, s), "finalize position 1"));
 
-    const size_t slab = (size_t)B * D * es;
+    const size_t slab = (size_t)B * d->d_model * es;
     for (int32_t t = 1; t <= N; ++t) {
-        const char* xt = (const char*)x + (size_t)(t - 1) * slab;
-        char* zt = (char*)z + (size_t)(t - 1) * slab;
-        char* kt = (char*)kc + (size_t)(t - 1) * slab;
-        char* vt = (char*)vc + (size_t)(t - 1) * slab;
-
-        // bf16 layers: W_o also stores h rounded to bf16 (the MLP's operand) and
-        // per-row partial sums of h^2; W_2 stores partial sums of z^2 (z as stored).
-        // The next GEMM turns those sums into its RMS row scale.
-        const bool b16 = dt == RT_BF16;
-        const int32_t parts = D / kRowSSTile;
-
-        GemmArgs go{};  // h = x_t + rho W_o a_t
-        go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
-        go.R = xt; go.ldr = D; go.rscale = d->residual_scale; go.M = B; go.N = D; go.K = D;
-        if (b16) { go.C2 = base + L.hb; go.rss_out = (float*)(base + L.hss); }
-        RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "output projection"));
-
-        GemmArgs g1{};  // g = GELU(W_1 RMS_mlp(h))
-        g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = w1; g1.C[0] = g;
-        g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = B; g1.N = F; g1.K = D;
-        if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
-        RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, g1, s), "mlp up"));
-
-        GemmArgs g2{};  // z_t = h + rho W_2 g
-        g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = zt; g2.ldc = D; g2.seg_n = D;
-        g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = B; g2.N = D; g2.K = F;
-        if (b16) g2.rss_out = (float*)(base + L.zss);
-        RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, g2, s), "mlp down"));
-
-        GemmArgs gk{};  // persistent pair of position t from the output z_t
-        gk.A = zt; gk.lda = D; gk.W[0] = wk; gk.W[1] = wv; gk.C[0] = kt; gk.C[1] = vt;
-        gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = B; gk.N = 2 * D; gk.K = D;
-        if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
-        RT_TRY(run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection"));
-
-        if (t < N) {
+        const size_t at = (size_t)(t - 1) * slab;
+        RT_TRY(enqueue_tail(d, w, p, base, L, B, a, (const char*)x + at, (char*)z + at, (char*)kc + at,
+                            (char*)vc + at, run));
+        if (t == N) break;
+        if (mode == Mode::Blocked) {
             // blocked step t, finishing query t+1 into a (its last merge)
             const int32_t b = block_of(t);
             u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
             u.init = (b == t); u.fin = 1;
             RT_TRY(run.check(launch_update(dt, dh, u, s), "blocked update"));
+        } else {
+            // naive step: query t+1 reads every pair 1..t at once, then its ephemeral pair
+            u.kv0 = 0; u.nkv = t; u.q0 = t; u.nq = 1; u.init = 1; u.fin = 1;
+            RT_TRY(run.check(launch_update(dt, dh, u, s), "naive step"));
         }
     }
     return RT_OK;
+}
+
+// One position n_past+1 against caches holding the pairs of positions 1..n_past.
+rt_status enqueue_decode(const rt_layer_desc* d, const rt_layer_weights* w, int32_t n_past, const void* x, void* z,
+                         void* kc, void* vc, void* ws, hipStream_t s, bool debug) {
+    using namespace rt;
+    Launcher run{s, debug};
+    const rt_dtype dt = d->attn.dtype;
+    const int32_t B = d->attn.batch, H = d->attn.n_heads;
+    const Layout L = layout_of(d, Mode::Decode);
+    char* base = (char*)ws;
+    const size_t at = (size_t)n_past * B * d->d_model * elem_bytes(dt);
+    char *kt = (char*)kc + at, *vt = (char*)vc + at;
+    const bool transformer = (d->flags & RT_FLAG_TRANSFORMER) != 0;
+    Projections p;
+    RT_TRY(enqueue_fold(d, w, base, L, run, &p));
+    // a Transformer's pair of this position is its ephemeral pair: straight into the caches
+    void* ke = transformer ? (void*)kt : (void*)(base + L.ke);
+    void* ve = transformer ? (void*)vt : (void*)(base + L.ve);
+    RT_TRY(enqueue_qkv(d, p, x, B, base + L.q, ke, ve, run));
+    UpdateArgs u{};
+    u.q = base + L.q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = base + L.a;
+    u.P = (int64_t)B * H; u.sigma2 = d->attn.softmax_scale * kLog2eHost;
+    u.kv0 = 0; u.nkv = n_past; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
+    RT_TRY(run.check(launch_update(dt, d->attn.head_dim, u, s), "decode attention"));
+    return enqueue_tail(d, w, p, base, L, B, base + L.a, x, z, transformer ? nullptr : kt,
+                        transformer ? nullptr : vt, run);
 }
 
 }  // namespace
@@ -340,7 +453,27 @@ rt_status rt_update_finalize_step(const rt_attn_desc* desc, int32_t t, const voi
 
 size_t rt_layer_workspace_bytes(const rt_layer_desc* desc) {
     if (check_layer(desc) != RT_OK) return 0;
-    return layout_of(desc).total;
+    return layout_of(desc, mode_of(desc)).total;
+}
+
+size_t rt_layer_decode_workspace_bytes(const rt_layer_desc* desc) {
+    if (check_layer(desc) != RT_OK) return 0;
+    return layout_of(desc, Mode::Decode).total;
+}
+
+rt_status rt_layer_decode_step(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past,
+                               const void* x_t, void* z_t, void* k_cache, void* v_cache, void* workspace,
+                               size_t workspace_bytes, rt_stream_t stream) {
+    RT_TRY(check_layer(desc));
+    RT_TRY(check_layer_ptrs(w, x_t, z_t, k_cache, v_cache, workspace));
+    if (n_past < 0 || n_past >= desc->attn.seq_len)
+        return fail(RT_ERR_INVALID_ARG, "n_past=%d outside 0..%d (seq_len is the cache capacity)", n_past,
+                    desc->attn.seq_len - 1);
+    const size_t need = layout_of(desc, Mode::Decode).total;
+    if (workspace_bytes < need)
+        return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return enqueue_decode(desc, w, n_past, x_t, z_t, k_cache, v_cache, workspace, (hipStream_t)stream,
+                          (desc->flags & RT_FLAG_DEBUG_SYNC) != 0);
 }
 
 rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w, const void* x, void* z,
@@ -348,7 +481,7 @@ rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w,
                            rt_stream_t stream) {
     RT_TRY(check_layer(desc));
     RT_TRY(check_layer_ptrs(w, x, z, k_cache, v_cache, workspace));
-    const size_t need = layout_of(desc).total;
+    const size_t need = layout_of(desc, mode_of(desc)).total;
     if (workspace_bytes < need)
         return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     return enqueue_layer(desc, w, x, z, k_cache, v_cache, workspace, (hipStream_t)stream,
@@ -362,7 +495,7 @@ rt_status rt_layer_plan_create(const rt_layer_desc* desc, const rt_layer_weights
     *plan = nullptr;
     RT_TRY(check_layer(desc));
     RT_TRY(check_layer_ptrs(w, x, z, k_cache, v_cache, workspace));
-    const size_t need = layout_of(desc).total;
+    const size_t need = layout_of(desc, mode_of(desc)).total;
     if (workspace_bytes < need)
         return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
     hipStream_t cs;

@@ -337,7 +337,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
 
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32>
 static hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
-    dim3 grid((uint32_t)(g.N / BN), (uint32_t)((g.M + BM - 1) / BM));
+    const int64_t row_tiles = (g.M + BM - 1) / BM;
+    if (row_tiles > 65535) return hipErrorInvalidConfiguration;  // grid y limit
+    dim3 grid((uint32_t)(g.N / BN), (uint32_t)row_tiles);
     hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF>), grid, dim3(64 * WM * WN), 0, s, g);
     return hipGetLastError();
 }
@@ -382,16 +384,21 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
     const bool big = g.M >= 4096;
     // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
     // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave)
-    // keep all CUs busy; the up-front projection over N*B rows uses 128x128.
+    // keep all CUs busy; products over N*B rows (the up-front projection, and
+    // every product of the Transformer layer) use 128x128.
     switch (kind) {
         case GemmKind::QKV:
             return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D, 32>(g, s)
                        : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
-            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
-        case GemmKind::W1: return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
+            return big ? run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s)
+                       : run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
+        case GemmKind::W1:
+            return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, D, 32>(g, s)
+                       : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
-            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
+            return big ? run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s)
+                       : run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
         case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
     }
     return hipErrorInvalidValue;

@@ -34,6 +34,9 @@ struct UpdateArgs {
 };
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
+// Plain causal attention over nq positions: query row i attends key/value rows
+// 0..i of k/v and is written to row i of a_out ([nq][P][dh]); m/l/o unused.
+hipError_t launch_causal_attention(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
 
 // C[M][N] = epilogue(A[M][K] * W^T), W given as up to 3 column segments of
 // seg_n rows each ([seg_n][K] row-major), outputs likewise split.

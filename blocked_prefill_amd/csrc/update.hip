@@ -17,7 +17,8 @@ namespace rt {
 // group of DH/8 consecutive lanes, each holding 8 of the DH components.
 // Items are ordered pair-fastest, so neighbouring groups read neighbouring
 // 16-byte pieces of the position-major q / k / v / state slabs.
-template <typename T, int DH>
+// CAUSAL: plain causal attention, as in the MFMA kernel below.
+template <typename T, int DH, bool CAUSAL>
 __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
     constexpr int G = DH / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -39,7 +40,8 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
     float mb = -INFINITY, lb = 0.f, ob[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const T* kp = (const T*)a.k + (int64_t)a.kv0 * slab + off;
     const T* vp = (const T*)a.v + (int64_t)a.kv0 * slab + off;
-    for (int s = 0; s < a.nkv; ++s) {
+    const int nkv = CAUSAL ? (int)j + 1 : a.nkv;
+    for (int s = 0; s < nkv; ++s) {
         float kv[8], vv[8];
         load8(kp + s * slab, kv);
         load8(vp + s * slab, vv);
@@ -56,6 +58,13 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
         mb = mn;
     }
 
+    if constexpr (CAUSAL) {
+        const float inv = 1.0f / lb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ob[e] *= inv;
+        store8((T*)a.a_out + j * slab + off, ob);
+        return;
+    }
     // merge with the stored state of this query
     const int64_t sidx = j * a.P + p;
     if (!a.init) {
@@ -118,7 +127,11 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // and the O^T rescale are lane-local (the two lanes q and q+32 share a query).
 // Blocks are dispatched so that all query tiles of a pair land on the same
 // XCD back to back, keeping the pair's keys/values in that XCD's L2.
-template <int WAVES>
+//
+// CAUSAL: plain causal attention (the Transformer layer's). Keys are the
+// queries' own positions (kv0 = q0 = 0); query i takes key rows 0..i and is
+// written to row i of a_out; no state is read or written.
+template <int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, int nqt) {
     constexpr int DH = 64;
     constexpr int KT = 64;          // key/value positions per LDS tile
@@ -148,6 +161,8 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     const int wave_q0 = qtile * 32 * WAVES + wave * 32;
     const bool wave_active = wave_q0 < a.nq;
     const int qrow = wave_q0 + ql;
+    // keys of this block: a causal tile needs those up to its last query
+    const int nkv = CAUSAL ? min(a.nq, (qtile + 1) * 32 * WAVES) : a.nkv;
     const bool qvalid = qrow < a.nq;
     const int64_t j = (int64_t)a.q0 + qrow;
 
@@ -183,34 +198,38 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     static_assert(KCH >= 1 && VCH >= 1 && (KT * 8) % NT == 0 && ((KT / 2) * 8) % NT == 0, "tile staging");
     bf16x8 kreg[KCH], vreg[VCH][2];
     auto fetch = [&](int kt0) {
-        const int rows = (a.nkv - kt0) < KT ? (a.nkv - kt0) : KT;  // 32 or 64
+        const int rows = (nkv - kt0) < KT ? (nkv - kt0) : KT;
+        // rows past the block (a ragged last tile) are zero: their scores are masked and
+        // their values must not be NaN
+        bf16x8 zero;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int c = tid + NT * i, r = c >> 3, ch = (c & 7) * 8;
-            if (r < rows) kreg[i] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
+            kreg[i] = r < rows ? *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch) : zero;
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
-            if (r0 < rows) {
-                vreg[i][0] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch);
-                vreg[i][1] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch);
-            }
+            vreg[i][0] = r0 < rows ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch) : zero;
+            vreg[i][1] = r0 + 1 < rows ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch)
+                                       : zero;
         }
     };
     fetch(0);
-    for (int kt0 = 0; kt0 < a.nkv; kt0 += KT) {
-        const int rows = (a.nkv - kt0) < KT ? (a.nkv - kt0) : KT;  // 32 or 64
+    for (int kt0 = 0; kt0 < nkv; kt0 += KT) {
+        const int rows = (nkv - kt0) < KT ? (nkv - kt0) : KT;  // 1..64 (64 except the last tile)
         lds_fence_barrier();  // the previous tile's LDS reads are done
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
             const int c = tid + NT * i, r = c >> 3, ch = (c & 7) * 8;
-            if (r < rows) *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + ch]) = kreg[i];
+            *reinterpret_cast<bf16x8*>(&Ks[r * KSTR + ch]) = kreg[i];
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
-            if (r0 < rows) {
+            {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
@@ -222,9 +241,10 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             }
         }
         lds_fence_barrier();  // this tile is in LDS
-        if (kt0 + KT < a.nkv) fetch(kt0 + KT);
+        if (kt0 + KT < nkv) fetch(kt0 + KT);
         if (!wave_active) continue;
         for (int c32 = 0; c32 < rows; c32 += 32) {
+            if (CAUSAL && kt0 + c32 > wave_q0 + 31) break;  // past this wave's last query
             f32x16 s;
 #pragma unroll
             for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -237,6 +257,28 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             // scaled maximum is sigma2 times it); the reference point m_run only
             // moves when some query's maximum exceeds it by more than 8 (base 2),
             // so the O^T rescale is skipped by the whole wave most of the time.
+            // ragged last tile: key rows at or past `rows` do not exist; causal: nor
+            // keys after the lane's query (bit e of `live`)
+            uint32_t live = 0xffffu;
+            if (CAUSAL && kt0 + c32 + 31 > wave_q0) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int kv = kt0 + c32 + (e & 7) + 8 * g + 16 * (e >> 3);
+                    if (kv > qrow || kv >= nkv) {
+                        s[e] = -INFINITY;
+                        live &= ~(1u << e);
+                    }
+                }
+            } else if (c32 + 32 > rows) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int kv = (e & 7) + 8 * g + 16 * (e >> 3);  // key row of score e (see krow)
+                    if (c32 + kv >= rows) {
+                        s[e] = -INFINITY;
+                        live &= ~(1u << e);
+                    }
+                }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
@@ -257,8 +299,10 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             bf16x8 p0, p1;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pa = fast_exp2(__builtin_fmaf(s[e], sigma2, -m_run));
-                const float pb = fast_exp2(__builtin_fmaf(s[e + 8], sigma2, -m_run));
+                float pa = fast_exp2(__builtin_fmaf(s[e], sigma2, -m_run));
+                float pb = fast_exp2(__builtin_fmaf(s[e + 8], sigma2, -m_run));
+                if (!(live & (1u << e))) pa = 0.f;  // (also when softmax_scale is 0)
+                if (!(live & (1u << (e + 8)))) pb = 0.f;
                 ps += pa + pb;
                 p0[e] = (bf16)pa;
                 p1[e] = (bf16)pb;
@@ -276,6 +320,22 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     if (!qvalid) return;
 
     // this lane holds dh = blk*32 + 8*ee + 4*g + (0..3) for blk in {0,1}, ee in 0..3 (accumulator e = 4*ee + i)
+    if constexpr (CAUSAL) {
+        const float inv = 1.0f / l_run;
+        bf16* out = (bf16*)a.a_out + j * slab + pair * DH;
+#pragma unroll
+        for (int ee = 0; ee < 4; ++ee) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int dh0 = blk * 32 + 8 * ee + 4 * g;
+                bf16x4 r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = (bf16)((blk ? o1[4 * ee + i] : o0[4 * ee + i]) * inv);
+                *reinterpret_cast<bf16x4*>(out + dh0) = r;
+            }
+        }
+        return;
+    }
     const int64_t sidx = j * a.P + pair;
     float* orow = a.o + sidx * DH;
     if (!a.init) {
@@ -345,29 +405,29 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     }
 }
 
-template <int WAVES>
+template <int WAVES, bool CAUSAL = false>
 static hipError_t launch_mfma(const UpdateArgs& a, hipStream_t s) {
     const int nqt = (a.nq + 32 * WAVES - 1) / (32 * WAVES);
     const int64_t blocks = a.P * nqt;
-    hipLaunchKernelGGL((update_mfma_kernel<WAVES>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a, nqt);
+    hipLaunchKernelGGL((update_mfma_kernel<WAVES, CAUSAL>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a, nqt);
     return hipGetLastError();
 }
 
-template <typename T, int DH>
+template <typename T, int DH, bool CAUSAL>
 static hipError_t launch_simt(const UpdateArgs& a, hipStream_t s) {
     const int64_t threads = (int64_t)a.nq * a.P * (DH / 8);
     if (threads <= 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((update_simt_kernel<T, DH>), dim3((uint32_t)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((update_simt_kernel<T, DH, CAUSAL>), dim3((uint32_t)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool CAUSAL>
 static hipError_t launch_typed(int head_dim, const UpdateArgs& a, hipStream_t s) {
     switch (head_dim) {
-        case 32: return launch_simt<T, 32>(a, s);
-        case 64: return launch_simt<T, 64>(a, s);
-        case 128: return launch_simt<T, 128>(a, s);
+        case 32: return launch_simt<T, 32, CAUSAL>(a, s);
+        case 64: return launch_simt<T, 64, CAUSAL>(a, s);
+        case 128: return launch_simt<T, 128, CAUSAL>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -377,13 +437,19 @@ constexpr int kMfmaMinBlock = 32;
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
-    if (dt == RT_BF16 && head_dim == 64 && a.nkv >= kMfmaMinBlock && (a.nkv % 32) == 0) {
+    if (dt == RT_BF16 && head_dim == 64 && a.nkv >= kMfmaMinBlock) {
         const int waves_needed = (a.nq + 31) / 32;
         if (waves_needed <= 1) return launch_mfma<1>(a, s);
         if (waves_needed <= 2) return launch_mfma<2>(a, s);
         return launch_mfma<4>(a, s);
     }
-    return dt == RT_BF16 ? launch_typed<bf16>(head_dim, a, s) : launch_typed<float>(head_dim, a, s);
+    return dt == RT_BF16 ? launch_typed<bf16, false>(head_dim, a, s) : launch_typed<float, false>(head_dim, a, s);
+}
+
+hipError_t launch_causal_attention(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
+    if (a.nq <= 0) return hipSuccess;
+    if (dt == RT_BF16 && head_dim == 64) return launch_mfma<4, true>(a, s);
+    return dt == RT_BF16 ? launch_typed<bf16, true>(head_dim, a, s) : launch_typed<float, true>(head_dim, a, s);
 }
 
 }  // namespace rt

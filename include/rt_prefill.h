@@ -59,6 +59,16 @@ typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
 
 /* flags of rt_layer_desc */
 #define RT_FLAG_DEBUG_SYNC 1u   /* synchronise and check after every launch (slow; for debugging) */
+/* The naive schedule (reading note, summary section 4.1): after position t,
+ * query t+1 reads all persistent pairs 1..t in one pass. Same result as the
+ * blocked schedule up to rounding order, with Theta(N^2) traffic; kept as
+ * the comparison point of the translated paper's Figure 4. */
+#define RT_FLAG_NAIVE_SCHEDULE 2u
+/* The standard Transformer layer (translated paper section 2.1): the pair
+ * stored at position t comes from the layer input x_t (it is the ephemeral
+ * pair), so all positions are computed at once with causal attention. The
+ * Figure 4 baseline. Excludes RT_FLAG_NAIVE_SCHEDULE. */
+#define RT_FLAG_TRANSFORMER 4u
 
 /* Attention shape. softmax_scale (finite, >= 0) multiplies every score <k, q>
  * (the pages' operator has none, i.e. 1.0; workloads use 1/sqrt(head_dim)). */
@@ -164,10 +174,42 @@ size_t rt_layer_workspace_bytes(const rt_layer_desc* desc);
  *   workspace: device memory of at least rt_layer_workspace_bytes(desc),
  *              256-byte aligned; its contents are scratch.
  * The B sequences are independent (no exchange between batch rows).
+ * desc->flags selects the schedule (blocked by default, RT_FLAG_NAIVE_SCHEDULE)
+ * or the standard Transformer layer (RT_FLAG_TRANSFORMER); the workspace
+ * size depends on that choice.
  */
 rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w,
                            const void* x, void* z, void* k_cache, void* v_cache,
                            void* workspace, size_t workspace_bytes, rt_stream_t stream);
+
+/*
+ * rt_layer_decode_workspace_bytes -- device workspace of rt_layer_decode_step
+ * (independent of seq_len and n_past), or 0 for an invalid descriptor.
+ */
+size_t rt_layer_decode_workspace_bytes(const rt_layer_desc* desc);
+
+/*
+ * rt_layer_decode_step -- autoregressive decoding of one new position
+ * t = n_past + 1 per sequence against the persistent KV cache a prefill (or
+ * earlier decode steps) left behind (translated paper section 7.3: each new
+ * token attends to keys and values cached from the earlier tokens, the same
+ * per-token work as a Transformer's decode). The layer map of one position
+ * of rt_layer_forward:
+ *   q, k', v' from x_t; a_t = attention over cached pairs 1..n_past and (k'_t, v'_t);
+ *   z_t = the layer's output; the persistent pair (k_t, v_t) from z_t is
+ *   appended at row n_past of the caches (with RT_FLAG_TRANSFORMER: (k'_t, v'_t)).
+ *   desc->attn.seq_len: the caches' capacity in positions; 0 <= n_past < seq_len
+ *   x_t     [B][d]          input of the new position (dtype), read
+ *   z_t     [B][d]          output (dtype), written
+ *   k_cache [seq_len][B][H][dh], v_cache likewise (dtype): rows 0..n_past-1
+ *           read, row n_past written, later rows untouched
+ *   workspace: at least rt_layer_decode_workspace_bytes(desc), 256-byte aligned.
+ * n_past = 0 is the first position (a_1 = v'_1). RT_FLAG_NAIVE_SCHEDULE has
+ * no effect here (one position has one schedule).
+ */
+rt_status rt_layer_decode_step(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past,
+                               const void* x_t, void* z_t, void* k_cache, void* v_cache,
+                               void* workspace, size_t workspace_bytes, rt_stream_t stream);
 
 /*
  * Plans: the same computation as rt_layer_forward, with its O(N) launches

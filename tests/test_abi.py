@@ -126,6 +126,55 @@ def test_workspace_bytes(lib):
     assert rt.rt_layer_workspace_bytes(_layer(d_ff=100)) == 0  # bf16 needs multiples of 128
 
 
+def test_workspace_bytes_of_the_other_modes(lib):
+    n, b, h, dh, f = 16, 2, 2, 64, 256
+    D = h * dh
+    al = lambda x: (x + 255) // 256 * 256
+    weights = 3 * al(D * D * 2) + al(f * D * 2)
+
+    def tail(rows):  # a, h, g, hb, hss, zss
+        return al(rows * D * 2) + al(rows * D * 4) + al(rows * f * 2) + al(rows * D * 2) \
+            + 2 * al(D // 32 * rows * 4 + 4)
+    # naive schedule: no online-softmax state
+    naive = 3 * al(n * b * D * 2) + tail(b) + weights
+    assert rt.rt_layer_workspace_bytes(_layer(flags=rt.RT_FLAG_NAIVE_SCHEDULE)) == naive
+    # Transformer: queries only (pairs go to the caches), every buffer over N*B rows
+    tf = al(n * b * D * 2) + tail(n * b) + weights
+    assert rt.rt_layer_workspace_bytes(_layer(flags=rt.RT_FLAG_TRANSFORMER)) == tf
+    # decode: one position, independent of seq_len and of the flags
+    dec = 3 * al(b * D * 2) + tail(b) + weights
+    for flags in (0, rt.RT_FLAG_TRANSFORMER, rt.RT_FLAG_NAIVE_SCHEDULE):
+        assert rt.rt_layer_decode_workspace_bytes(_layer(flags=flags)) == dec
+    assert rt.rt_layer_decode_workspace_bytes(_layer(attn=_attn(seq_len=4096))) == dec
+    both = rt.RT_FLAG_NAIVE_SCHEDULE | rt.RT_FLAG_TRANSFORMER
+    assert rt.rt_layer_workspace_bytes(_layer(flags=both)) == 0
+    assert rt.rt_layer_workspace_bytes(_layer(flags=64)) == 0
+
+
+def test_flags_are_validated(lib):
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    for flags, text in ((rt.RT_FLAG_NAIVE_SCHEDULE | rt.RT_FLAG_TRANSFORMER, "exclude"), (8, "unknown flags")):
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_layer_forward(_layer(flags=flags), W, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+        assert e.value.status == 1 and text in str(e.value)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    d = _layer()
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    need = rt.rt_layer_decode_workspace_bytes(d)
+    for n_past in (-1, 16, 17):  # seq_len 16 is the caches' capacity
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_layer_decode_step(d, W, n_past, FAKE, FAKE, FAKE, FAKE, FAKE, need, stream=0)
+        assert e.value.status == 1 and "n_past" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_decode_step(d, W, 3, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_decode_step(d, W, 3, FAKE, None, FAKE, FAKE, FAKE, need, stream=0)
+    assert "z is NULL" in str(e.value)
+
+
 def test_layer_rejects_bad_arguments(lib):
     d = _layer()
     W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
