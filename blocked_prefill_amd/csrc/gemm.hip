@@ -65,28 +65,38 @@ __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1)
 // written to a double-buffered swizzled LDS tile, and multiplied with
 // v_mfma_f32_32x32x16_bf16; each wave computes a (BM/WM) x (BN/WN) block.
 // One LDS-only barrier per K tile.
-template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
+//
+// KS > 1 splits K inside the workgroup: KS groups of WM*WN waves each run the
+// pipeline above over their own contiguous K range, with their own LDS
+// buffers, and the KS partial tiles are added in LDS before the epilogue. At
+// the per-position shapes (M = batch) this multiplies the waves per tile and
+// divides the serial K-loop length without any cross-workgroup reduction.
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g) {
     // MF = 32: v_mfma_f32_32x32x16_bf16 blocks; MF = 16: v_mfma_f32_16x16x32_bf16 blocks
     // (four times as many independent accumulators for the same wave tile).
     static_assert(MF == 32 || MF == 16, "MFMA block");
-    constexpr int NT = 64 * WM * WN;
+    static_assert(KS == 1 || !(FLAGS & EPI_RMS), "the self-summed row norm needs the whole K range");
+    constexpr int NTG = 64 * WM * WN;  // threads of one K group
+    constexpr int NT = NTG * KS;
     constexpr int BK = 64;
     constexpr int TMW = BM / WM, TNW = BN / WN;
     constexpr int FM = TMW / MF, FN = TNW / MF;
     typedef typename std::conditional<MF == 32, f32x16, f32x4>::type acc_t;
     constexpr int AE = MF == 32 ? 16 : 4;  // accumulator elements per lane
     constexpr int A_CH = BM * (BK / 8), W_CH = BN * (BK / 8);  // 16-byte chunks per tile
-    constexpr int LA = A_CH / NT, LW = W_CH / NT;               // chunks per thread per tile
+    constexpr int LA = A_CH / NTG, LW = W_CH / NTG;             // chunks per thread per tile
     constexpr int STAGE = (A_CH + W_CH) * 16;
-    static_assert(FM >= 1 && FN >= 1 && A_CH % NT == 0 && W_CH % NT == 0, "tile shape");
+    static_assert(FM >= 1 && FN >= 1 && A_CH % NTG == 0 && W_CH % NTG == 0, "tile shape");
     static_assert(D >= 2, "prefetch depth");
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char smem_all[KS * 2 * STAGE];
     __shared__ float rs[BM];     // row scale (1/rms)
     __shared__ float rsum[BM];   // row partial sums of squares of the stored output
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = tid / NTG, gtid = tid % NTG, wave = gtid >> 6;
+    char* const smem = smem_all + grp * 2 * STAGE;  // this K group's double buffer
     const int wm = wave / WN, wn = wave % WN;
     const int gq = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
@@ -112,12 +122,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
         }
     }
 
-    // this thread's chunks: slot s = NT*i + tid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
+    // this thread's chunks: slot s = NTG*i + gtid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
     const bf16* a_src[LA];
     int a_slot[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int s = NT * i + tid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+        const int s = NTG * i + gtid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
         int64_t row = m0 + r;
         row = row < g.M ? row : g.M - 1;  // rows past M read a valid row; their results are dropped
         a_src[i] = A + row * g.lda + c * 8;
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     const bf16* w_src[LW];
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
-        const int s = NT * i + tid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
+        const int s = NTG * i + gtid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
         w_src[i] = W + (int64_t)r * g.K + c * 8;
     }
 
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < LA; ++i) *reinterpret_cast<bf16x8*>(base + a_slot[i] * 16) = ra[u][i];
 #pragma unroll
-        for (int i = 0; i < LW; ++i) *reinterpret_cast<bf16x8*>(base + (A_CH + NT * i + tid) * 16) = rw[u][i];
+        for (int i = 0; i < LW; ++i) *reinterpret_cast<bf16x8*>(base + (A_CH + NTG * i + gtid) * 16) = rw[u][i];
     };
 
     acc_t acc[FM][FN];
@@ -161,10 +171,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     auto compute = [&](int buf) {
         const char* sA = smem + buf * STAGE;
         const char* sW = sA + A_CH * 16;
-        constexpr int KS = MF == 32 ? 16 : 32;  // k per MFMA
-        constexpr int GPS = KS / 8;             // 16-byte chunks per MFMA k-slice
+        constexpr int KM = MF == 32 ? 16 : 32;  // k per MFMA
+        constexpr int GPS = KM / 8;             // 16-byte chunks per MFMA k-slice
 #pragma unroll
-        for (int kk = 0; kk < BK / KS; ++kk) {
+        for (int kk = 0; kk < BK / KM; ++kk) {
             const int c = GPS * kk + lgrp;
             bf16x8 aop[FM], wop[FN];
 #pragma unroll
@@ -194,16 +204,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     };
 
     // The K loop is branch-free so that the compiler's wait counts stay exact
-    // (the host guarantees KT % D == 0): prefetches past the last tile reload
-    // the last tile, and the one spare store lands in the LDS buffer nobody
-    // reads again.
-    const int KT = g.K / BK;
-    const int last = (KT - 1) * BK;
+    // (the host guarantees (K/64/KS) % D == 0): prefetches past the last tile
+    // reload the last tile, and the one spare store lands in the LDS buffer
+    // nobody reads again. K group grp covers K tiles [grp*KT, (grp+1)*KT).
+    const int KT = g.K / BK / KS;
+    const int k_first = grp * KT * BK;
+    const int last = k_first + (KT - 1) * BK;
     // prologue: tiles 0..D-1 in flight, tile 0 in LDS buffer 0, tile D replaces it in the ring
 #pragma unroll
-    for (int u = 0; u < D; ++u) load(u, min(u * BK, last));
+    for (int u = 0; u < D; ++u) load(u, min(k_first + u * BK, last));
     store(0, 0);
-    load(0, min(D * BK, last));
+    load(0, min(k_first + D * BK, last));
     for (int kt0 = 0; kt0 < KT; kt0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
             compute(kt & 1);
             const int nu = (u + 1) % D;    // ring stage of tile kt+1 (constant once unrolled)
             store(nu, (kt + 1) & 1);
-            load(nu, min((kt + 1 + D) * BK, last));
+            load(nu, min(k_first + (kt + 1 + D) * BK, last));
         }
     }
 
@@ -243,14 +254,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     // stores and residual loads, and each 32-column group's sum of squares is a
     // 4-lane shuffle.
     constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
-    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes)
+    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes);
+    // each K group stages its partial tile in its own buffers
     constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : BM / 2;
     static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
     constexpr int CPRW = BN / 8;               // 8-column runs per row
-    constexpr int RUNS = PR * CPRW / NT;       // runs per thread per pass
-    static_assert((PR * CPRW) % NT == 0 && NT % CPRW == 0, "runs divide evenly");
+    constexpr int RUNS = (PR * CPRW + NT - 1) / NT;  // runs per thread per pass
+    static_assert(NT % CPRW == 0 && CPRW % 4 == 0, "runs map onto lanes evenly");
     static_assert(!(FLAGS & EPI_ROWSS) || (BN % kRowSSTile == 0 && CPRW >= 4), "32-column groups");
-    float* tl = reinterpret_cast<float*>(smem);
+    float* tl = reinterpret_cast<float*>(smem);          // this group's partial tile
+    const float* tl0 = reinterpret_cast<const float*>(smem_all);
     TC* C = (TC*)g.C[seg];
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
@@ -270,18 +283,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < RUNS; ++it) {
-        const int x = tid + NT * it;
+        // (a run past the tile, when NT does not divide the run count, is computed
+        // on row 0 and dropped: every lane takes part in the shuffles below)
+        const int xr = tid + NT * it;
+        const bool in_tile = xr < PR * CPRW;
+        const int x = in_tile ? xr : xr % CPRW;
         const int rl = x / CPRW, c0 = (x % CPRW) * 8;
         const int r = pass * PR + rl;
         const int64_t row = m0 + r;
-        const bool ok = row < g.M;
+        const bool ok = in_tile && row < g.M;
         const int col = n0 + c0;
-        float v[8];
-        {
-            const float4 p0 = *reinterpret_cast<const float4*>(&tl[rl * LDT + c0]);
-            const float4 p1 = *reinterpret_cast<const float4*>(&tl[rl * LDT + c0 + 4]);
-            v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-            v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kg = 0; kg < KS; ++kg) {
+            const float* t = tl0 + kg * (2 * STAGE / 4) + rl * LDT + c0;
+            const float4 p0 = *reinterpret_cast<const float4*>(t);
+            const float4 p1 = *reinterpret_cast<const float4*>(t + 4);
+            v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
+            v[4] += p1.x; v[5] += p1.y; v[6] += p1.z; v[7] += p1.w;
         }
         if (FLAGS & (EPI_RMS | EPI_RMS_PARTS)) {
             const float sc = rs[r];
@@ -335,12 +354,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_kernel(GemmArgs g) {
     }
 }
 
-template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32>
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32, int KS = 1>
 static hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
     const int64_t row_tiles = (g.M + BM - 1) / BM;
     if (row_tiles > 65535) return hipErrorInvalidConfiguration;  // grid y limit
     dim3 grid((uint32_t)(g.N / BN), (uint32_t)row_tiles);
-    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF>), grid, dim3(64 * WM * WN), 0, s, g);
+    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>), grid, dim3(64 * WM * WN * KS), 0,
+                       s, g);
     return hipGetLastError();
 }
 
@@ -379,29 +399,51 @@ bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K) {
     return (K % 64 == 0) && (N % 128 == 0);
 }
 
-template <int D>
+template <int D, int KS>
 static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
     const bool big = g.M >= 4096;
     // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
-    // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave)
-    // keep all CUs busy; products over N*B rows (the up-front projection, and
-    // every product of the Transformer layer) use 128x128.
+    // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave),
+    // with K split over 2 or 4 wave groups where that measured faster (W_2,
+    // W_o, W_kv); products over N*B rows (the up-front projection, and every
+    // product of the Transformer layer) use 128x128.
     switch (kind) {
         case GemmKind::QKV:
-            return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D, 32>(g, s)
-                       : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
+            if constexpr (KS == 1)
+                return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D, 32>(g, s)
+                           : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
+            break;
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
-            return big ? run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s)
-                       : run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
+            if (big) {
+                if constexpr (KS == 1)
+                    return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s);
+                break;
+            }
+            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
         case GemmKind::W1:
-            return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, D, 32>(g, s)
-                       : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
+            if constexpr (KS == 1)
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, D, 32>(g, s)
+                           : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
+            break;
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
-            return big ? run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s)
-                       : run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16>(g, s);
-        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
+            if (big) {
+                if constexpr (KS == 1) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s);
+                break;
+            }
+            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
     }
     return hipErrorInvalidValue;
+}
+
+// K groups per workgroup for a kind and shape: the measured choice when K
+// divides into an even number of 64-wide tiles per group, else fewer.
+static int k_groups(GemmKind kind, const GemmArgs& g) {
+    if (g.M >= 4096) return 1;
+    int ks = kind == GemmKind::W2 ? 4 : (kind == GemmKind::WO || kind == GemmKind::KV) ? 2 : 1;
+    const int kt = g.K / 64;
+    while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
+    return ks;
 }
 
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s) {
@@ -415,10 +457,17 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
         }
         return hipErrorInvalidValue;
     }
-    // K is a multiple of 128 (so the 64-wide K-tile count is even); prefetch 4 tiles ahead when it divides by 4
+    // K is a multiple of 128 (an even number of 64-wide K tiles); each K group
+    // prefetches 4 tiles ahead when its tile count divides by 4, else 2
     if ((g.K / 64) % 2) return hipErrorInvalidValue;
-    if ((g.K / 64) % 4 == 0) return dispatch_bf16<4>(kind, g, s);
-    return dispatch_bf16<2>(kind, g, s);
+    const int ks = k_groups(kind, g);
+    const bool d4 = (g.K / 64 / ks) % 4 == 0;
+    switch (ks) {
+        case 1: return d4 ? dispatch_bf16<4, 1>(kind, g, s) : dispatch_bf16<2, 1>(kind, g, s);
+        case 2: return d4 ? dispatch_bf16<4, 2>(kind, g, s) : dispatch_bf16<2, 2>(kind, g, s);
+        case 4: return d4 ? dispatch_bf16<4, 4>(kind, g, s) : dispatch_bf16<2, 4>(kind, g, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------- gain folding

@@ -13,6 +13,27 @@
 
 namespace rt {
 
+// 8 consecutive elements as loaded (converted to fp32 only where used, so that
+// a batch of loads can be issued before the first wait).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    bf16x8 r;
+    __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float operator[](int e) const { return (float)r[e]; }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int e) const {
+        const float4& h = e < 4 ? a : b;
+        const int k = e & 3;
+        return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    }
+};
+
 // SIMT update: one item = (query row i, batch*head pair p), handled by a
 // group of DH/8 consecutive lanes, each holding 8 of the DH components.
 // Items are ordered pair-fastest, so neighbouring groups read neighbouring
@@ -106,6 +127,101 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
     }
 }
 
+// SIMT update for the blocked schedule's smallest steps (blocks of U = 1, 2
+// or 4 pairs), where a launch's time is the latency of its memory round
+// trips. Items as in update_simt_kernel, with blockIdx.y the query row.
+// One round trip per step: the code between the first load and the last
+// merge has no branch, so the query, the U keys/values, the stored state and
+// the ephemeral pair are all requested at once. Merges that do not apply (no
+// stored state, no ephemeral pair) are merges of weight zero: their score is
+// -inf, taken after the block's first key has made the running maximum
+// finite, and their values are zeroed (their addresses fall back to the
+// query's own, a valid location).
+template <typename T, int DH, int U>
+__global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
+    constexpr int G = DH / 8;
+    const int64_t pg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair * G + lane
+    if (pg >= a.P * G) return;  // whole groups leave together
+    const int64_t p = pg / G;
+    const int lane = (int)(pg % G);
+    const int64_t slab = a.P * DH;  // elements per position
+    const int64_t off = p * DH + lane * 8;
+    const T* kp = (const T*)a.k + (int64_t)a.kv0 * slab + off;
+    const T* vp = (const T*)a.v + (int64_t)a.kv0 * slab + off;
+
+    for (int64_t i = blockIdx.y; i < a.nq; i += gridDim.y) {
+        const int64_t j = a.q0 + i;
+        const int64_t sidx = j * a.P + p;
+        const bool merge_state = !a.init;
+        const bool finish = a.fin && i == 0;
+        const T* qp = (const T*)a.q + j * slab + off;
+
+        Raw8<T> qr, ker, ver, kr[U], vr[U];
+        Raw8<float> osr;
+        qr.load(qp);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            kr[u].load(kp + u * slab);
+            vr[u].load(vp + u * slab);
+        }
+        const float* sp = merge_state ? a.m + sidx : (const float*)qp;
+        const float* lp = merge_state ? a.l + sidx : (const float*)qp;
+        const float ms_ld = *sp, ls_ld = *lp;
+        osr.load(merge_state ? a.o + sidx * DH + lane * 8 : (const float*)a.q);
+        ker.load(finish ? (const T*)a.k_eph + j * slab + off : qp);
+        ver.load(finish ? (const T*)a.v_eph + j * slab + off : qp);
+
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = qr[e] * a.sigma2;
+
+        float mb = -INFINITY, lb = 0.f, ob[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        auto merge = [&](float d, const Raw8<T>& val) {
+            const float mn = fmaxf(mb, d);
+            const float c = fast_exp2(mb - mn);
+            const float pe = fast_exp2(d - mn);
+            lb = lb * c + pe;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] = ob[e] * c + pe * val[e];
+            mb = mn;
+        };
+        auto score = [&](const Raw8<T>& key) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qv[e] * key[e];
+            return group_sum<G>(d);
+        };
+#pragma unroll
+        for (int u = 0; u < U; ++u) merge(score(kr[u]), vr[u]);  // the block (mb finite after u = 0)
+        {  // the position's own ephemeral pair (weight zero unless finishing)
+            const float d = score(ker);
+            merge(finish ? d : -INFINITY, ver);
+        }
+        {  // the stored state (weight zero on first touch)
+            const float ms = merge_state ? ms_ld : -INFINITY;
+            const float ls = merge_state ? ls_ld : 0.f;
+            const float mn = fmaxf(ms, mb);
+            const float cs = fast_exp2(ms - mn), cb = fast_exp2(mb - mn);
+            lb = ls * cs + lb * cb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] = (merge_state ? osr[e] : 0.f) * cs + ob[e] * cb;
+            mb = mn;
+        }
+        if (finish) {  // a = o / l
+            const float inv = 1.0f / lb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] *= inv;
+            store8((T*)a.a_out + off, ob);
+        } else {
+            if (lane == 0) {
+                a.m[sidx] = mb;
+                a.l[sidx] = lb;
+            }
+            store8(a.o + sidx * DH + lane * 8, ob);
+        }
+    }
+}
+
 // Workgroup barrier ordering LDS accesses only: global loads stay in flight across it.
 __device__ __forceinline__ void lds_fence_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -128,10 +244,12 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // Blocks are dispatched so that all query tiles of a pair land on the same
 // XCD back to back, keeping the pair's keys/values in that XCD's L2.
 //
+// RAGGED: the block length need not be a multiple of 32 (decode, naive
+// schedule); the missing key rows of the last chunk are masked.
 // CAUSAL: plain causal attention (the Transformer layer's). Keys are the
 // queries' own positions (kv0 = q0 = 0); query i takes key rows 0..i and is
 // written to row i of a_out; no state is read or written.
-template <int WAVES, bool CAUSAL>
+template <int WAVES, bool RAGGED, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, int nqt) {
     constexpr int DH = 64;
     constexpr int KT = 64;          // key/value positions per LDS tile
@@ -198,23 +316,20 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     static_assert(KCH >= 1 && VCH >= 1 && (KT * 8) % NT == 0 && ((KT / 2) * 8) % NT == 0, "tile staging");
     bf16x8 kreg[KCH], vreg[VCH][2];
     auto fetch = [&](int kt0) {
-        const int rows = (nkv - kt0) < KT ? (nkv - kt0) : KT;
-        // rows past the block (a ragged last tile) are zero: their scores are masked and
-        // their values must not be NaN
-        bf16x8 zero;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+        // rows past the block (a ragged last tile) repeat its last row: real,
+        // finite data whose scores are masked (weight exactly 0). The loads are
+        // unconditional so that they stay in flight across the tile's work.
+        const int last = ((nkv - kt0) < KT ? (nkv - kt0) : KT) - 1;
 #pragma unroll
         for (int i = 0; i < KCH; ++i) {
-            const int c = tid + NT * i, r = c >> 3, ch = (c & 7) * 8;
-            kreg[i] = r < rows ? *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch) : zero;
+            const int c = tid + NT * i, r = min(c >> 3, last), ch = (c & 7) * 8;
+            kreg[i] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
         }
 #pragma unroll
         for (int i = 0; i < VCH; ++i) {
             const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
-            vreg[i][0] = r0 < rows ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0) * slab + ch) : zero;
-            vreg[i][1] = r0 + 1 < rows ? *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + r0 + 1) * slab + ch)
-                                       : zero;
+            vreg[i][0] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0, last)) * slab + ch);
+            vreg[i][1] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0 + 1, last)) * slab + ch);
         }
     };
     fetch(0);
@@ -257,25 +372,21 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             // scaled maximum is sigma2 times it); the reference point m_run only
             // moves when some query's maximum exceeds it by more than 8 (base 2),
             // so the O^T rescale is skipped by the whole wave most of the time.
-            // ragged last tile: key rows at or past `rows` do not exist; causal: nor
-            // keys after the lane's query (bit e of `live`)
-            uint32_t live = 0xffffu;
-            if (CAUSAL && kt0 + c32 + 31 > wave_q0) {
+            // Masking (RAGGED: key rows at or past the block's end; CAUSAL: also
+            // keys after the lane's query) exists only in those instances: the
+            // blocked schedule's blocks are whole 32-row chunks.
+            uint32_t live = 0xffffu;  // bit e: score e is a real key
+            if constexpr (RAGGED || CAUSAL) {
+                const bool masked = CAUSAL ? kt0 + c32 + 31 > wave_q0 : c32 + 32 > rows;  // wave-uniform
+                if (masked) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int kv = kt0 + c32 + (e & 7) + 8 * g + 16 * (e >> 3);
-                    if (kv > qrow || kv >= nkv) {
-                        s[e] = -INFINITY;
-                        live &= ~(1u << e);
-                    }
-                }
-            } else if (c32 + 32 > rows) {
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int kv = (e & 7) + 8 * g + 16 * (e >> 3);  // key row of score e (see krow)
-                    if (c32 + kv >= rows) {
-                        s[e] = -INFINITY;
-                        live &= ~(1u << e);
+                    for (int e = 0; e < 16; ++e) {
+                        const int kv = c32 + (e & 7) + 8 * g + 16 * (e >> 3);  // key row of score e (see krow)
+                        const bool dead = CAUSAL ? (kt0 + kv > qrow || kt0 + kv >= nkv) : kv >= rows;
+                        if (dead) {
+                            s[e] = -INFINITY;
+                            live &= ~(1u << e);
+                        }
                     }
                 }
             }
@@ -301,8 +412,10 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             for (int e = 0; e < 8; ++e) {
                 float pa = fast_exp2(__builtin_fmaf(s[e], sigma2, -m_run));
                 float pb = fast_exp2(__builtin_fmaf(s[e + 8], sigma2, -m_run));
-                if (!(live & (1u << e))) pa = 0.f;  // (also when softmax_scale is 0)
-                if (!(live & (1u << (e + 8)))) pb = 0.f;
+                if constexpr (RAGGED || CAUSAL) {  // (zero also when softmax_scale is 0)
+                    if (!(live & (1u << e))) pa = 0.f;
+                    if (!(live & (1u << (e + 8)))) pb = 0.f;
+                }
                 ps += pa + pb;
                 p0[e] = (bf16)pa;
                 p1[e] = (bf16)pb;
@@ -409,14 +522,32 @@ template <int WAVES, bool CAUSAL = false>
 static hipError_t launch_mfma(const UpdateArgs& a, hipStream_t s) {
     const int nqt = (a.nq + 32 * WAVES - 1) / (32 * WAVES);
     const int64_t blocks = a.P * nqt;
-    hipLaunchKernelGGL((update_mfma_kernel<WAVES, CAUSAL>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a, nqt);
+    if (!CAUSAL && a.nkv % 32 != 0)
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, true, false>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a,
+                           nqt);
+    else
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, false, CAUSAL>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s,
+                           a, nqt);
     return hipGetLastError();
 }
 
 template <typename T, int DH, bool CAUSAL>
 static hipError_t launch_simt(const UpdateArgs& a, hipStream_t s) {
+    if (a.nq <= 0) return hipSuccess;
+    if constexpr (!CAUSAL && sizeof(T) == 2) {
+        // blocks of 1, 2 and 4 pairs (most steps of the blocked schedule): one round trip
+        if (a.nkv == 1 || a.nkv == 2 || a.nkv == 4) {
+            const dim3 grid((uint32_t)((a.P * (DH / 8) + 255) / 256), (uint32_t)(a.nq < 65535 ? a.nq : 65535));
+            if (a.nkv == 1)
+                hipLaunchKernelGGL((update_small_kernel<T, DH, 1>), grid, dim3(256), 0, s, a);
+            else if (a.nkv == 2)
+                hipLaunchKernelGGL((update_small_kernel<T, DH, 2>), grid, dim3(256), 0, s, a);
+            else
+                hipLaunchKernelGGL((update_small_kernel<T, DH, 4>), grid, dim3(256), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     const int64_t threads = (int64_t)a.nq * a.P * (DH / 8);
-    if (threads <= 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL((update_simt_kernel<T, DH, CAUSAL>), dim3((uint32_t)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
@@ -433,7 +564,7 @@ static hipError_t launch_typed(int head_dim, const UpdateArgs& a, hipStream_t s)
 }
 
 // Blocks of at least this many pairs go to the MFMA kernel (bf16, head_dim 64).
-constexpr int kMfmaMinBlock = 32;
+constexpr int kMfmaMinBlock = 16;
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
