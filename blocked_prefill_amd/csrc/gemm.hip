@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
 
     __shared__ __attribute__((aligned(16))) char smem_all[KS * 2 * STAGE];
     __shared__ float rs[BM];     // row scale (1/rms)
-    __shared__ float rsum[BM];   // row partial sums of squares of the stored output
+    __shared__ float qsum[(FLAGS & EPI_RMS_PARTS) ? BM * 16 : 1];  // per-quad sums of the RMS partials
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int grp = tid / NTG, gtid = tid % NTG, wave = gtid >> 6;
@@ -104,23 +104,6 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     const int seg = n0 / g.seg_n;
     const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * g.K;
     const bf16* A = (const bf16*)g.A;
-
-    // partial sums of squares of this tile's A rows (EPI_RMS_PARTS), laid out
-    // [M][n_parts] with n_parts % 4 == 0 and <= 64: fetched now as float4s,
-    // combined after the main loop.
-    constexpr int PQ = (BM * 16 + NT - 1) / NT;  // float4 quads per thread
-    float4 pss[(FLAGS & EPI_RMS_PARTS) ? PQ : 1];
-    const int qpr = g.n_parts / 4;                // quads per row
-    if (FLAGS & EPI_RMS_PARTS) {
-#pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int idx = tid + NT * i, r = idx / qpr;
-            const int64_t row = m0 + r;
-            pss[i] = (r < BM && row < g.M)
-                         ? reinterpret_cast<const float4*>(g.rss_in + row * g.n_parts)[idx % qpr]
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
 
     // this thread's chunks: slot s = NTG*i + gtid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
     const bf16* a_src[LA];
@@ -215,6 +198,61 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     for (int u = 0; u < D; ++u) load(u, min(k_first + u * BK, last));
     store(0, 0);
     load(0, min(k_first + D * BK, last));
+    // partial sums of squares of this tile's A rows (EPI_RMS_PARTS), laid out
+    // [M][n_parts] with n_parts % 4 == 0 and <= 64: fetched as float4s behind
+    // the first K tiles (so the main loop's first waits do not include them),
+    // combined after the main loop.
+    constexpr int PQ = (BM * 16 + NT - 1) / NT;  // float4 quads per thread
+    float4 pss[(FLAGS & EPI_RMS_PARTS) ? PQ : 1];
+    const int qpr = g.n_parts / 4;                // quads per row
+    if (FLAGS & EPI_RMS_PARTS) {
+        // unconditional loads (rows clamped into the tile and the matrix): a
+        // conditional load would make the compiler wait for every load in
+        // flight where the branches join; quads past the tile are dropped later
+#pragma unroll
+        for (int i = 0; i < PQ; ++i) {
+            const int idx = tid + NT * i, r = min(idx / qpr, BM - 1);
+            const int64_t row = min(m0 + r, g.M - 1);
+            pss[i] = reinterpret_cast<const float4*>(g.rss_in + row * g.n_parts)[idx % qpr];
+        }
+    }
+
+    constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
+    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes);
+    // each K group stages its partial tile in its own buffers
+    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : BM / 2;
+    static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
+    constexpr int CPRW = BN / 8;               // 8-column runs per row
+    constexpr int RUNS = (PR * CPRW + NT - 1) / NT;  // runs per thread per pass
+    // The epilogue's run of a thread: (pass, it) -> tile row rl of the pass and
+    // first column c0 (a run past the tile, when NT does not divide the run
+    // count, is computed on row 0 and dropped: every lane takes part in the
+    // shuffles of the epilogue).
+    auto run_of = [&](int it, int& rl, int& c0) {
+        const int xr = tid + NT * it;
+        const int x = xr < PR * CPRW ? xr : xr % CPRW;
+        rl = x / CPRW;
+        c0 = (x % CPRW) * 8;
+        return xr < PR * CPRW;
+    };
+    // Residual rows of the epilogue, when a thread has few runs: loaded now,
+    // unconditionally (rows clamped into the matrix), so their latency hides
+    // under the main loop.
+    constexpr int NPASS = BM / PR;
+    constexpr bool PREF_R = (FLAGS & EPI_RESID) && NPASS * RUNS <= 2;
+    Raw8<TR> res_pre[PREF_R ? NPASS * RUNS : 1];
+    if constexpr (PREF_R) {
+#pragma unroll
+        for (int pass = 0; pass < NPASS; ++pass)
+#pragma unroll
+            for (int it = 0; it < RUNS; ++it) {
+                int rl, c0;
+                run_of(it, rl, c0);
+                const int64_t row = min(m0 + pass * PR + rl, g.M - 1);
+                res_pre[pass * RUNS + it].load((const TR*)g.R + row * g.ldr + n0 + c0);
+            }
+    }
+
     for (int kt0 = 0; kt0 < KT; kt0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
@@ -228,15 +266,18 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     }
 
     if (FLAGS & EPI_RMS_PARTS) {
-        for (int r = tid; r < BM; r += NT) rsum[r] = 0.f;
-        __syncthreads();
+        // each quad's sum to LDS, then one thread per row adds its row's quads
 #pragma unroll
         for (int i = 0; i < PQ; ++i) {
             const int idx = tid + NT * i, r = idx / qpr;
-            if (r < BM) atomicAdd(&rsum[r], (pss[i].x + pss[i].y) + (pss[i].z + pss[i].w));
+            if (r < BM) qsum[r * 16 + idx % qpr] = (pss[i].x + pss[i].y) + (pss[i].z + pss[i].w);
         }
         __syncthreads();
-        for (int r = tid; r < BM; r += NT) rs[r] = rsqrtf(rsum[r] / (float)g.K + g.eps);
+        for (int r = tid; r < BM; r += NT) {
+            float v = 0.f;
+            for (int q = 0; q < qpr; ++q) v += qsum[r * 16 + q];
+            rs[r] = rsqrtf(v / (float)g.K + g.eps);
+        }
     }
     if (FLAGS & EPI_RMS) {
         if (wn == 0) {
@@ -253,13 +294,6 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     // each thread then owns runs of 8 consecutive columns of one row: 16-byte
     // stores and residual loads, and each 32-column group's sum of squares is a
     // 4-lane shuffle.
-    constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
-    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes);
-    // each K group stages its partial tile in its own buffers
-    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : BM / 2;
-    static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
-    constexpr int CPRW = BN / 8;               // 8-column runs per row
-    constexpr int RUNS = (PR * CPRW + NT - 1) / NT;  // runs per thread per pass
     static_assert(NT % CPRW == 0 && CPRW % 4 == 0, "runs map onto lanes evenly");
     static_assert(!(FLAGS & EPI_ROWSS) || (BN % kRowSSTile == 0 && CPRW >= 4), "32-column groups");
     float* tl = reinterpret_cast<float*>(smem);          // this group's partial tile
@@ -283,12 +317,9 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     __syncthreads();
 #pragma unroll
     for (int it = 0; it < RUNS; ++it) {
-        // (a run past the tile, when NT does not divide the run count, is computed
-        // on row 0 and dropped: every lane takes part in the shuffles below)
-        const int xr = tid + NT * it;
-        const bool in_tile = xr < PR * CPRW;
-        const int x = in_tile ? xr : xr % CPRW;
-        const int rl = x / CPRW, c0 = (x % CPRW) * 8;
+        int rl, c0;
+        const bool in_tile = run_of(it, rl, c0);
+        const int x = rl * CPRW + c0 / 8;  // run index within the pass (4 consecutive lanes per 32 columns)
         const int r = pass * PR + rl;
         const int64_t row = m0 + r;
         const bool ok = in_tile && row < g.M;
@@ -311,7 +342,11 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
         }
-        if ((FLAGS & EPI_RESID) && ok) {
+        if constexpr (PREF_R) {
+            const Raw8<TR>& res = res_pre[pass * RUNS + it];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = res[e] + g.rscale * v[e];
+        } else if ((FLAGS & EPI_RESID) && ok) {
             float res[8];
             load8((const TR*)g.R + row * g.ldr + col, res);
 #pragma unroll
@@ -406,7 +441,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
     // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave),
     // with K split over 2 or 4 wave groups where that measured faster (W_2,
     // W_o, W_kv); products over N*B rows (the up-front projection, and every
-    // product of the Transformer layer) use 128x128.
+    // product of the Transformer layer) use 128x128, prefetching 2 K tiles
+    // ahead in the tall products with fp32 operands in the epilogue (register
+    // budget: 2 waves per SIMD).
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1)
@@ -414,24 +451,26 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
                            : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
             break;
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
-            if (big) {
-                if constexpr (KS == 1)
-                    return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s);
-                break;
+            if constexpr (KS == 1) {
+                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(g, s);
             }
-            return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+            if constexpr (KS <= 2)
+                if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+            break;
         case GemmKind::W1:
             if constexpr (KS == 1)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, D, 32>(g, s)
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(g, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
             break;
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
-            if (big) {
-                if constexpr (KS == 1) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32>(g, s);
-                break;
+            if constexpr (KS == 1) {
+                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(g, s);
             }
-            return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
-        case GemmKind::KV: return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
+            if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+            break;
+        case GemmKind::KV:
+            if constexpr (KS <= 2) return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
+            break;
     }
     return hipErrorInvalidValue;
 }

@@ -39,6 +39,27 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// 8 consecutive elements as loaded (converted to fp32 only where used, so that
+// a batch of loads can be issued before the first wait).
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16> {
+    bf16x8 r;
+    __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
+    __device__ __forceinline__ float operator[](int e) const { return (float)r[e]; }
+};
+template <> struct Raw8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = reinterpret_cast<const float4*>(p)[0];
+        b = reinterpret_cast<const float4*>(p)[1];
+    }
+    __device__ __forceinline__ float operator[](int e) const {
+        const float4& h = e < 4 ? a : b;
+        const int k = e & 3;
+        return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
+    }
+};
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f32(float x);

@@ -13,26 +13,6 @@
 
 namespace rt {
 
-// 8 consecutive elements as loaded (converted to fp32 only where used, so that
-// a batch of loads can be issued before the first wait).
-template <typename T> struct Raw8;
-template <> struct Raw8<bf16> {
-    bf16x8 r;
-    __device__ __forceinline__ void load(const bf16* p) { r = *reinterpret_cast<const bf16x8*>(p); }
-    __device__ __forceinline__ float operator[](int e) const { return (float)r[e]; }
-};
-template <> struct Raw8<float> {
-    float4 a, b;
-    __device__ __forceinline__ void load(const float* p) {
-        a = reinterpret_cast<const float4*>(p)[0];
-        b = reinterpret_cast<const float4*>(p)[1];
-    }
-    __device__ __forceinline__ float operator[](int e) const {
-        const float4& h = e < 4 ? a : b;
-        const int k = e & 3;
-        return k == 0 ? h.x : k == 1 ? h.y : k == 2 ? h.z : h.w;
-    }
-};
 
 // SIMT update: one item = (query row i, batch*head pair p), handled by a
 // group of DH/8 consecutive lanes, each holding 8 of the DH components.
@@ -229,7 +209,8 @@ __device__ __forceinline__ void lds_fence_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// MFMA update for blocks of b >= 32 pairs, head_dim 64, bf16 (gfx950).
+// MFMA update for blocks of b >= 32 pairs (any length >= 32 with the RAGGED
+// instance), head_dim 64, bf16 (gfx950).
 //
 // A workgroup of WAVES waves takes one (batch*head pair p, tile of 32*WAVES
 // queries); each wave owns 32 queries. The block's keys and values stream
@@ -564,7 +545,7 @@ static hipError_t launch_typed(int head_dim, const UpdateArgs& a, hipStream_t s)
 }
 
 // Blocks of at least this many pairs go to the MFMA kernel (bf16, head_dim 64).
-constexpr int kMfmaMinBlock = 16;
+constexpr int kMfmaMinBlock = 32;
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
