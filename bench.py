@@ -70,7 +70,75 @@ def measured_traffic():
         return None
 
 
-def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True):
+def traffic_summary(fetch_dir, write_dir):
+    """Summary of two rocprofv3 counter passes over `bench.py --counters` (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch): each counter calibrated on the run's final
+    1 GiB device copy, then averaged over the 2047 update launches just before it.
+    Prints the text kept under profiles/ (with the update kernels' source hash)."""
+    import csv
+    import hashlib
+
+    def rows(d, counter):
+        out = []
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if r["Counter_Name"] == counter:
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        return sorted(out)
+
+    fetch, write = rows(fetch_dir, "FETCH_SIZE"), rows(write_dir, "WRITE_SIZE")
+    copy_bytes = 1 << 30
+
+    def calibrate(rs):
+        i = max(k for k, (_, name, _) in enumerate(rs) if "copy" in name.lower())
+        factor = copy_bytes / (rs[i][2] * 1024)
+        ups = [v for _, name, v in rs[:i] if "update_" in name][-2047:]
+        return factor, rs[i][2], ups
+
+    ff, fk, fu = calibrate(fetch)
+    wf, wk, wu = calibrate(write)
+    assert len(fu) == len(wu) == 2047, (len(fu), len(wu))
+    N, P, dh, s_ = 2048, 512 * 16, 64, 2
+    meas = [fu[t - 1] * 1024 * ff + wu[t - 1] * 1024 * wf for t in range(1, N)]
+    alg = [update_bytes(t, N, P, dh, s_) for t in range(1, N)]
+    rd = sum(fu) * 1024 * ff / 2047
+    wr = sum(wu) * 1024 * wf / 2047
+    src = os.path.join(ROOT, "blocked_prefill_amd", "csrc", "update.hip")
+    per_b = []
+    b = 1
+    while b < N:
+        ts = [t for t in range(1, N) if t & -t == b]
+        per_b.append(f"b={b} {sum(meas[t - 1] for t in ts) / sum(alg[t - 1] for t in ts):.3f}")
+        b *= 2
+    lines = [
+        "# HBM traffic of the fused blocked-update kernels, one layer of the 6-layer stack workload",
+        "# (B=512, N=2048, d_model=1024, 16 heads x 64, bf16): 2047 launches (t = 1..2047).",
+        "#",
+        "# Commands (repository root, one MI355X; two passes, one counter each; then the summary):",
+        "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch -o run -- python3 bench.py --counters",
+        "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write -o run -- python3 bench.py --counters",
+        "#   python3 bench.py --traffic-summary gpurun_out/fetch gpurun_out/write",
+        "# bench.py --counters runs one layer forward, then that layer's 2047 update launches",
+        "# (the ones counted here), then a plain 1 GiB device copy (the calibration kernel).",
+        "#",
+        f"# Calibration on the 1 GiB copy ({copy_bytes} bytes read, {copy_bytes} written):",
+        f"#   FETCH_SIZE = {fk:.0f} KiB  -> bytes read    = FETCH_SIZE * 1024 * {ff:.4f}",
+        f"#   WRITE_SIZE = {wk:.0f} KiB  -> bytes written = WRITE_SIZE * 1024 * {wf:.4f}",
+        "#",
+        "# Per launch, averaged over the 2047 update launches (calibrated):",
+        f"#   read {rd / 1e6:.2f} MB + written {wr / 1e6:.2f} MB = {(rd + wr) / 1e6:.2f} MB;  algorithmic model "
+        f"{sum(alg) / 2047 / 1e6:.2f} MB;  ratio {(rd + wr) / (sum(alg) / 2047):.3f}",
+        "# Per block size b (measured / algorithmic):",
+        "#   " + "  ".join(per_b[:6]),
+        "#   " + "  ".join(per_b[6:]),
+        "#",
+        "# Kernel source these counters were taken on (bench.py reports traffic only while it matches):",
+        f"source_sha256 = {hashlib.sha256(open(src, 'rb').read()).hexdigest()}",
+        f"bytes_per_launch = {round(rd + wr, -4):.0f}",
+    ]
+    print("\n".join(lines))
+
+
+def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True, t_range=None):
     """Replay one layer's fused update steps t = 1..N-1 on the workspace's q, k', v' and state
     (offsets as laid out by the library: q, k', v', m, l, o first). With timing_torch, each
     launch is bracketed by HIP events on the launch stream; returns per-launch ms."""
@@ -90,7 +158,7 @@ def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_t
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(N - 1)] if timed else None
     if sync:
         torch.cuda.synchronize()
-    for t in range(1, N):
+    for t in range(*(t_range or (1, N))):
         if timed:
             starts[t - 1].record(stream)
         rt.rt_update_finalize_step(attn, t, base + off_q, base + off_ke, base + off_ve, k_cache, v_cache,
@@ -225,10 +293,14 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="single-layer latency at B=512, d=1024 for N = 256..2048: RT blocked, RT naive, "
                          "Transformer (log-log slopes)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter passes over --counters (no GPU needed)")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
     args = ap.parse_args()
 
+    if args.traffic_summary:
+        return traffic_summary(*args.traffic_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (batch rows are independent; "
               "a multi-GPU run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
@@ -274,14 +346,25 @@ def main():
     vs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
 
     if args.counters:
-        # one layer forward (fills q, k', v' and the KV cache), then its update sequence, then the copy
-        rt.rt_layer_forward(desc, weights[0], x, zs[0], ks[0], vs[0], ws, stream=stream)
-        update_sequence(rt, attn, ws, ks[0], vs[0], N, B, H, D, stream, None)
+        # q, k', v' (the workspace's first three slabs) and the KV cache filled with
+        # random values (memory traffic does not depend on them; a whole layer forward
+        # would be ~12k dispatches, each serialised by the counter collection), then
+        # the layer's 2047 update launches, then the calibration copy
+        slab = N * B * D
+        qkv = torch.empty(0, dtype=torch.bfloat16, device=dev).set_(
+            ws.untyped_storage(), 0, (3, slab), (((slab * 2 + 255) // 256 * 256) // 2, 1))
+        qkv.normal_()
+        ks[0].normal_()
+        vs[0].normal_()
+        torch.cuda.synchronize()
+        for t0 in range(1, N, 256):
+            update_sequence(rt, attn, ws, ks[0], vs[0], N, B, H, D, stream, None, t_range=(t0, min(t0 + 256, N)))
+            log(f"counters: update launches t={t0}..{min(t0 + 255, N - 1)} done")
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-        log("counters run done: layer forward, 2047 update launches, 1 GiB copy")
+        log("counters run done: 2047 update launches, 1 GiB copy")
         return
 
     t0 = time.time()
@@ -350,7 +433,7 @@ def main():
         achieved = byts.mean() / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                    "kernel": "update_simt_kernel<bf16,64> (fused blocked update + finalize)",
+                    "kernel": "fused blocked update + finalize (update_small / update_simt / update_mfma kernels)",
                     "launches": N - 1, "avg_launch_us": round(avg_s * 1e6, 2),
                     "alg_bytes_per_launch": int(byts.mean())}
         levels = {}
