@@ -30,11 +30,11 @@ class _Cfg(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_double), ("residual_scale", ctypes.c_double),
                 ("rms_eps", ctypes.c_double), ("kv_from_input", ctypes.c_int32),
-                ("round_bf16", ctypes.c_int32)]
+                ("round_bf16", ctypes.c_int32), ("qk_norm", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
-    _fields_ = [(n, _fp) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")]
+    _fields_ = [(n, _fp) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp", "g_q", "g_k")]
 
 
 class _Out(ctypes.Structure):
@@ -135,11 +135,13 @@ def attention_at(q, k_eph, v_eph, k, v, softmax_scale: float, positions) -> np.n
 
 def layer_forward(x, weights: dict, *, n_heads: int, softmax_scale: float, residual_scale: float = 1.0,
                   rms_eps: float = 1e-6, kv_from_input: bool = False, round_bf16: bool = False,
-                  want=("z", "k", "v")) -> dict:
+                  qk_norm: bool = False, want=("z", "k", "v")) -> dict:
     """Naive RT layer on x [N][R][d] (fp32 values). Returns float64 outputs by name.
 
     Names: z, k, v, q, k_eph, v_eph, a, h ([N][R][d]); g ([N][R][F]); and
     always x_next (float32, z as stored: the next layer's input).
+    qk_norm: every query and key RMS-normalised per head (gains g_q, g_k of the
+    weights, ones when absent).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     N, R, d = x.shape
@@ -147,10 +149,10 @@ def layer_forward(x, weights: dict, *, n_heads: int, softmax_scale: float, resid
     if d % n_heads:
         raise ValueError("d_model must be a multiple of n_heads")
     cfg = _Cfg(N, R, d, n_heads, d // n_heads, F, softmax_scale, residual_scale, rms_eps,
-               int(bool(kv_from_input)), int(bool(round_bf16)))
+               int(bool(kv_from_input)), int(bool(round_bf16)), int(bool(qk_norm)))
     keep = {}
     wp = {}
-    for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp"):
+    for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp", "g_q", "g_k"):
         if weights.get(n) is None:
             wp[n] = ctypes.cast(None, _fp)
         else:

@@ -70,8 +70,10 @@ def attention(q, k_eph, v_eph, k, v, softmax_scale):
     return a
 
 
-def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1e-6, kv_from_input=False):
-    """Blocked-schedule RT layer in float64 on x [N][R][d]. Returns z, k, v (float64)."""
+def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1e-6, kv_from_input=False,
+                  qk_norm=False):
+    """Blocked-schedule RT layer in float64 on x [N][R][d]. Returns z, k, v (float64).
+    qk_norm: queries and keys RMS-normalised per head (gains g_q, g_k)."""
     x = np.asarray(x, dtype=np.float64)
     n, rows, d = x.shape
     dh = d // n_heads
@@ -80,8 +82,11 @@ def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1
     g_mlp = W.get("g_mlp", np.ones(d))
     # every query and ephemeral pair depends only on the input: formed up front
     u = _rms(x, g_attn, rms_eps)
-    q = (u @ W["w_q"].T).reshape(n, rows, n_heads, dh)
-    k_eph = (u @ W["w_k"].T).reshape(n, rows, n_heads, dh)
+    g_q = W.get("g_q", np.ones(d)).reshape(n_heads, dh)
+    g_k = W.get("g_k", np.ones(d)).reshape(n_heads, dh)
+    head_rms = (lambda y, g: _rms(y, g, rms_eps)) if qk_norm else (lambda y, g: y)
+    q = head_rms((u @ W["w_q"].T).reshape(n, rows, n_heads, dh), g_q)
+    k_eph = head_rms((u @ W["w_k"].T).reshape(n, rows, n_heads, dh), g_k)
     v_eph = (u @ W["w_v"].T).reshape(n, rows, n_heads, dh)
     K = np.zeros((n, rows, n_heads, dh))
     V = np.zeros((n, rows, n_heads, dh))
@@ -95,7 +100,7 @@ def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1
         z[i] = h + rho * _gelu(_rms(h, g_mlp, rms_eps) @ W["w_1"].T) @ W["w_2"].T
         src = x[i] if kv_from_input else z[i]
         us = _rms(src, g_attn, rms_eps)
-        K[i] = (us @ W["w_k"].T).reshape(rows, n_heads, dh)
+        K[i] = head_rms((us @ W["w_k"].T).reshape(rows, n_heads, dh), g_k)
         V[i] = (us @ W["w_v"].T).reshape(rows, n_heads, dh)
         (k0, k1), (q0, q1) = step(t, n)
         for j in range(q0, q1 + 1):

@@ -243,6 +243,7 @@ typedef struct {
     double softmax_scale, residual_scale, rms_eps;
     int32_t kv_from_input; /* 0: persistent pair from z_t (RT); 1: from x_t (Transformer) */
     int32_t round_bf16;    /* round the stored tensors to bf16 */
+    int32_t qk_norm;       /* RMS-normalise each head's query and key (ephemeral and persistent) */
 } rto_layer_cfg;
 
 typedef struct {
@@ -250,6 +251,7 @@ typedef struct {
     const float *w_1;                   /* [F][d] */
     const float *w_2;                   /* [d][F] */
     const float *g_attn, *g_mlp;        /* [d]; NULL means ones */
+    const float *g_q, *g_k;             /* [d] query / key norm gains (qk_norm); NULL means ones */
 } rto_weights;
 
 /* Outputs, each [n_pos][n_rows][width], values before their own rounding.
@@ -278,6 +280,10 @@ static void put(double* dst, size_t off, const double* src, int n) {
  *   z_t    = h + rho W_2 GELU(W_1 RMS_mlp(h))
  *   k_t, v_t = W_k RMS_attn(z_t), W_v RMS_attn(z_t)   (from x_t instead when
  *            kv_from_input is set, which is the standard Transformer layer)
+ * With qk_norm, every query and key (q, k', k) is RMS-normalised per head
+ * after its projection, with gains g_q, g_k (the "magenta" RMS of the
+ * translated paper's section 2 notation, read per head as in the query/key
+ * normalisation it cites).
  * Positions run in order; rows are independent, and the work inside each
  * position is split over rows and output features.
  */
@@ -316,6 +322,18 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
             const float* W = which == 0 ? w->w_q : (which == 1 ? w->w_k : w->w_v);
             /* q at 2d, k' at 3d, v' at 4d of each row's scratch */
             dot_rows(W + (size_t)oo * d, d, buf + d, per_row, R, buf + 2 * d + o, per_row);
+        }
+        if (c->qk_norm) {
+#pragma omp parallel for schedule(static)
+            for (int r = 0; r < R; ++r) {
+                double* b = buf + r * per_row;
+                for (int hh = 0; hh < H; ++hh) {
+                    double* qh = b + 2 * d + hh * dh;
+                    double* kh = b + 3 * d + hh * dh;
+                    rto_rmsnorm(qh, dh, w->g_q ? w->g_q + hh * dh : NULL, eps, qh);
+                    rto_rmsnorm(kh, dh, w->g_k ? w->g_k + hh * dh : NULL, eps, kh);
+                }
+            }
         }
         /* 2. attention of position t over persistent pairs 1..t-1 plus its own ephemeral pair */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -410,13 +428,24 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
                 for (int r = 0; r < nr; ++r) {
                     const size_t off = (size_t)t * Rd + (size_t)(r0 + r) * d + oo;
                     if (o < d) {
-                        if (out->k) out->k[off] = s[r];
-                        Kc[off] = keep(s[r], rb);
+                        buf[(size_t)(r0 + r) * per_row + 9 * d + oo] = s[r]; /* k, finished below */
                     } else {
                         if (out->v) out->v[off] = s[r];
                         Vc[off] = keep(s[r], rb);
                     }
                 }
+            }
+        }
+#pragma omp parallel for schedule(static)
+        for (int r = 0; r < R; ++r) {
+            double* kr = buf + r * per_row + 9 * d;
+            if (c->qk_norm)
+                for (int hh = 0; hh < H; ++hh)
+                    rto_rmsnorm(kr + hh * dh, dh, w->g_k ? w->g_k + hh * dh : NULL, eps, kr + hh * dh);
+            for (int i = 0; i < d; ++i) {
+                const size_t off = (size_t)t * Rd + (size_t)r * d + i;
+                if (out->k) out->k[off] = kr[i];
+                Kc[off] = keep(kr[i], rb);
             }
         }
         /* 6. report */

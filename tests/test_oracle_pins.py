@@ -158,20 +158,25 @@ def test_attention_blocked_equals_naive(n):
 
 # ---------------------------------------------------------------- the layer
 
-def _textbook_transformer_layer(x, w, n_heads, sigma, rho, eps):
-    """Pre-LN causal Transformer layer (section 2.1 of the translated paper) in torch fp64."""
+def _textbook_transformer_layer(x, w, n_heads, sigma, rho, eps, qk_norm=False):
+    """Pre-LN causal Transformer layer (section 2.1 of the translated paper) in torch fp64.
+    qk_norm: torch's RMS norm over each head's query and key, times gains g_q, g_k."""
     X = torch.from_numpy(x.astype(np.float64))                       # [N][R][d]
     W = {k: torch.from_numpy(v.astype(np.float64)) for k, v in w.items()}
     n, r, d = X.shape
     dh = d // n_heads
     u = F.rms_norm(X, (d,), weight=W["g_attn"], eps=eps)
-    heads = lambda y: y.reshape(n, r, n_heads, dh).permute(1, 2, 0, 3)  # [R][H][N][dh]
-    q, k, v = heads(F.linear(u, W["w_q"])), heads(F.linear(u, W["w_k"])), heads(F.linear(u, W["w_v"]))
+    split = lambda y: y.reshape(n, r, n_heads, dh)
+    norm = (lambda y, g: F.rms_norm(y, (dh,), eps=eps) * g.reshape(n_heads, dh)) if qk_norm else (lambda y, g: y)
+    heads = lambda y: y.permute(1, 2, 0, 3)                            # [R][H][N][dh]
+    kq = norm(split(F.linear(u, W["w_k"])), W.get("g_k"))
+    q = heads(norm(split(F.linear(u, W["w_q"])), W.get("g_q")))
+    k, v = heads(kq), heads(split(F.linear(u, W["w_v"])))
     a = F.scaled_dot_product_attention(q, k, v, is_causal=True, scale=sigma).permute(2, 0, 1, 3).reshape(n, r, d)
     h = X + rho * F.linear(a, W["w_o"])
     y = h + rho * F.linear(F.gelu(F.linear(F.rms_norm(h, (d,), weight=W["g_mlp"], eps=eps), W["w_1"])), W["w_2"])
     us = F.rms_norm(X, (d,), weight=W["g_attn"], eps=eps)
-    return {"z": y.numpy(), "k": F.linear(us, W["w_k"]).numpy(), "v": F.linear(us, W["w_v"]).numpy(),
+    return {"z": y.numpy(), "k": kq.reshape(n, r, d).numpy(), "v": F.linear(us, W["w_v"]).numpy(),
             "a": a.numpy(), "h": h.numpy()}
 
 
@@ -186,6 +191,42 @@ def test_layer_with_input_kv_is_the_textbook_transformer(n, r, d, h, f, rho):
     want = _textbook_transformer_layer(x, w, h, sigma, rho, 1e-6)
     for name in ("z", "k", "v", "a", "h"):
         assert _rel(got[name], want[name]) < 1e-12, name
+
+
+@pytest.mark.parametrize("n,r,d,h,f", [(1, 1, 16, 2, 32), (23, 2, 32, 4, 64), (30, 2, 64, 2, 128)])
+def test_qk_norm_layer_with_input_kv_is_the_textbook_transformer(n, r, d, h, f):
+    """The query/key norm (translated paper section 2 notation, per head) against
+    torch's RMS norm applied to each head of the textbook layer's q and k."""
+    rng = _rng(60 + n)
+    x = rng.standard_normal((n, r, d)).astype(np.float32)
+    w = _weights(rng, d, f)
+    w["g_q"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    w["g_k"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    sigma = 1.0 / math.sqrt(d // h)
+    got = oracle.layer_forward(x, w, n_heads=h, softmax_scale=sigma, rms_eps=1e-6, kv_from_input=True,
+                               qk_norm=True, want=("z", "k", "v", "a", "h"))
+    want = _textbook_transformer_layer(x, w, h, sigma, 1.0, 1e-6, qk_norm=True)
+    for name in ("z", "k", "v", "a", "h"):
+        assert _rel(got[name], want[name]) < 1e-12, name
+    if n > 1:  # (one position attends to its own pair only: no score matters)
+        plain = oracle.layer_forward(x, w, n_heads=h, softmax_scale=sigma, rms_eps=1e-6, kv_from_input=True)
+        assert _rel(plain["z"], want["z"]) > 1e-3  # the norm changes the layer
+
+
+def test_qk_norm_makes_the_layer_invariant_to_query_and_key_scale():
+    """With the per-head query/key norm, scaling W_q and W_k by positive constants
+    leaves the RT layer unchanged (up to the norm's epsilon); without it, not."""
+    rng = _rng(70)
+    n, r, d, h, f = 12, 2, 32, 4, 64
+    x = rng.standard_normal((n, r, d)).astype(np.float32)
+    w = _weights(rng, d, f)
+    w2 = dict(w, w_q=(w["w_q"] * 8).astype(np.float32), w_k=(w["w_k"] * 0.25).astype(np.float32))
+    kw = dict(n_heads=h, softmax_scale=0.3, rms_eps=1e-30)
+    a, b = oracle.layer_forward(x, w, qk_norm=True, **kw), oracle.layer_forward(x, w2, qk_norm=True, **kw)
+    for name in ("z", "k", "v"):
+        assert _rel(a[name], b[name]) < 1e-12, name
+    c, e = oracle.layer_forward(x, w, **kw), oracle.layer_forward(x, w2, **kw)
+    assert _rel(c["z"], e["z"]) > 1e-3
 
 
 def test_persistent_pair_comes_from_the_output():
@@ -214,14 +255,21 @@ def test_persistent_pair_comes_from_the_output():
     assert _rel(got["a"][1, 0], ((v1x + v2e) / 2).numpy()) > 1e-3
 
 
-@pytest.mark.parametrize("n,kv_in", [(1, False), (2, False), (3, False), (8, False), (37, False), (37, True), (64, False)])
-def test_layer_blocked_equals_naive(n, kv_in):
+@pytest.mark.parametrize("n,kv_in,qk", [(1, False, False), (2, False, False), (3, False, False), (8, False, False),
+                                        (37, False, False), (37, True, False), (64, False, False), (37, False, True),
+                                        (20, True, True)])
+def test_layer_blocked_equals_naive(n, kv_in, qk):
     rng = _rng(40 + n)
     d, h, f, r = 32, 2, 64, 2
     x = rng.standard_normal((n, r, d)).astype(np.float32)
     w = _weights(rng, d, f)
-    got = oracle.layer_forward(x, w, n_heads=h, softmax_scale=0.3, residual_scale=0.8, kv_from_input=kv_in)
-    want = blocked.layer_forward(x, w, n_heads=h, softmax_scale=0.3, residual_scale=0.8, kv_from_input=kv_in)
+    if qk:
+        w["g_q"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+        w["g_k"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    got = oracle.layer_forward(x, w, n_heads=h, softmax_scale=0.3, residual_scale=0.8, kv_from_input=kv_in,
+                               qk_norm=qk)
+    want = blocked.layer_forward(x, w, n_heads=h, softmax_scale=0.3, residual_scale=0.8, kv_from_input=kv_in,
+                                 qk_norm=qk)
     for name in ("z", "k", "v"):
         assert _rel(got[name], want[name]) <= 1e-12, name
 
