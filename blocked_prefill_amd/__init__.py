@@ -15,13 +15,14 @@ __all__ = [
     "rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes",
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
     "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_last_error", "EXPORTED",
-    "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER",
+    "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
 ]
 
 RT_F32, RT_BF16 = 0, 1
 RT_FLAG_DEBUG_SYNC = 1
 RT_FLAG_NAIVE_SCHEDULE = 2
 RT_FLAG_TRANSFORMER = 4
+RT_FLAG_QK_NORM = 8
 _STATUS = {0: "RT_OK", 1: "RT_ERR_INVALID_ARG", 2: "RT_ERR_UNSUPPORTED", 3: "RT_ERR_WORKSPACE", 4: "RT_ERR_HIP"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,7 +51,8 @@ class LayerDesc(ctypes.Structure):
 
 
 class LayerWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp", "g_q",
+                                               "g_k")]
 
 
 _lib = None
@@ -149,7 +151,8 @@ def rt_layer_workspace_bytes(desc: LayerDesc) -> int:
 def _weights(w) -> LayerWeights:
     if isinstance(w, LayerWeights):
         return w
-    return LayerWeights(**{n: _ptr(w.get(n)) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")})
+    return LayerWeights(**{n: _ptr(w.get(n)) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp",
+                                                        "g_q", "g_k")})
 
 
 def rt_layer_forward(desc: LayerDesc, weights, x, z, k_cache, v_cache, workspace, workspace_bytes=None,

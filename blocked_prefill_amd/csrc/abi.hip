@@ -64,8 +64,10 @@ rt_status check_layer(const rt_layer_desc* d) {
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers need d_model and d_ff multiples of 128");
     if ((d->flags & RT_FLAG_NAIVE_SCHEDULE) && (d->flags & RT_FLAG_TRANSFORMER))
         return fail(RT_ERR_INVALID_ARG, "RT_FLAG_NAIVE_SCHEDULE and RT_FLAG_TRANSFORMER exclude each other");
-    if (d->flags & ~(RT_FLAG_DEBUG_SYNC | RT_FLAG_NAIVE_SCHEDULE | RT_FLAG_TRANSFORMER))
+    if (d->flags & ~(RT_FLAG_DEBUG_SYNC | RT_FLAG_NAIVE_SCHEDULE | RT_FLAG_TRANSFORMER | RT_FLAG_QK_NORM))
         return fail(RT_ERR_INVALID_ARG, "unknown flags 0x%x", d->flags);
+    if ((d->flags & RT_FLAG_QK_NORM) && d->attn.dtype == RT_BF16 && d->attn.head_dim > 64)
+        return fail(RT_ERR_UNSUPPORTED, "the bf16 query/key norm supports head_dim 32 or 64");
     if (d->attn.dtype == RT_BF16 && d->d_model > 64 * rt::kRowSSTile)
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers support d_model up to %d", 64 * rt::kRowSSTile);
     return RT_OK;
@@ -164,7 +166,8 @@ rt_status check_layer_ptrs(const rt_layer_weights* w, const void* x, void* z, vo
         if (!aligned16(ps[i])) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
     }
     if (((uintptr_t)ws & 255u) != 0) return fail(RT_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-    if ((w->g_attn && !aligned16(w->g_attn)) || (w->g_mlp && !aligned16(w->g_mlp)))
+    if ((w->g_attn && !aligned16(w->g_attn)) || (w->g_mlp && !aligned16(w->g_mlp)) ||
+        (w->g_q && !aligned16(w->g_q)) || (w->g_k && !aligned16(w->g_k)))
         return fail(RT_ERR_INVALID_ARG, "gains must be 16-byte aligned");
     return RT_OK;
 }
@@ -197,9 +200,10 @@ rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* 
     return RT_OK;
 }
 
-// q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x.
-rt_status enqueue_qkv(const rt_layer_desc* d, const Projections& p, const void* x, int64_t rows, void* q, void* ke,
-                      void* ve, Launcher& run) {
+// q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x (with the query/key
+// norm on q and k' when the layer has it).
+rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, const void* x,
+                      int64_t rows, void* q, void* ke, void* ve, Launcher& run) {
     using namespace rt;
     const int32_t D = d->d_model;
     GemmArgs gq{};
@@ -208,6 +212,10 @@ rt_status enqueue_qkv(const rt_layer_desc* d, const Projections& p, const void* 
     gq.C[0] = q; gq.C[1] = ke; gq.C[2] = ve;
     gq.ldc = D; gq.seg_n = D; gq.eps = d->rms_eps;
     gq.M = rows; gq.N = 3 * D; gq.K = D;
+    if (d->flags & RT_FLAG_QK_NORM) {
+        gq.qkn_mask = 3; gq.head_dim = d->attn.head_dim;
+        gq.qkn_gain[0] = w->g_q; gq.qkn_gain[1] = w->g_k;
+    }
     return run.check(launch_gemm(d->attn.dtype, GemmKind::QKV, gq, run.s), "qkv projection");
 }
 
@@ -252,6 +260,7 @@ rt_status enqueue_tail(const rt_layer_desc* d, const rt_layer_weights* w, const 
     gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = kt; gk.C[1] = vt;
     gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
     if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
+    if (d->flags & RT_FLAG_QK_NORM) { gk.qkn_mask = 1; gk.head_dim = d->attn.head_dim; gk.qkn_gain[0] = w->g_k; }
     return run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection");
 }
 
@@ -266,7 +275,7 @@ rt_status enqueue_transformer(const rt_layer_desc* d, const rt_layer_weights* w,
     char* base = (char*)ws;
     Projections p;
     RT_TRY(enqueue_fold(d, w, base, L, run, &p));
-    RT_TRY(enqueue_qkv(d, p, x, rows, base + L.q, kc, vc, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, rows, base + L.q, kc, vc, run));
     UpdateArgs u{};
     u.q = base + L.q; u.k = kc; u.v = vc; u.a_out = base + L.a;
     u.P = (int64_t)d->attn.batch * d->attn.n_heads; u.nq = d->attn.seq_len;
@@ -293,7 +302,7 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
     RT_TRY(enqueue_fold(d, w, base, L, run, &p));
 
     // every query and ephemeral pair depends only on the input: one GEMM up front
-    RT_TRY(enqueue_qkv(d, p, x, (int64_t)N * B, q, ke, ve, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, (int64_t)N * B, q, ke, ve, run));
 
     UpdateArgs u{};
     u.q = q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = a;
@@ -343,7 +352,7 @@ rt_status enqueue_decode(const rt_layer_desc* d, const rt_layer_weights* w, int3
     // a Transformer's pair of this position is its ephemeral pair: straight into the caches
     void* ke = transformer ? (void*)kt : (void*)(base + L.ke);
     void* ve = transformer ? (void*)vt : (void*)(base + L.ve);
-    RT_TRY(enqueue_qkv(d, p, x, B, base + L.q, ke, ve, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, B, base + L.q, ke, ve, run));
     UpdateArgs u{};
     u.q = base + L.q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = base + L.a;
     u.P = (int64_t)B * H; u.sigma2 = d->attn.softmax_scale * kLog2eHost;

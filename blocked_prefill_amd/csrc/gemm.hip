@@ -342,6 +342,20 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
         }
+        if constexpr ((FLAGS & EPI_QKNORM) != 0) {
+            // per-head RMS (query/key norm): a head's head_dim/8 runs sit in as many
+            // consecutive lanes (BN is a multiple of head_dim); seg is uniform per workgroup
+            if ((g.qkn_mask >> seg) & 1) {
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+                for (int o = 1; o < g.head_dim / 8; o <<= 1) ss += __shfl_xor(ss, o, 64);
+                const float sc = rsqrtf(ss / (float)g.head_dim + g.eps);
+                const float* gg = g.qkn_gain[seg];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= sc * (gg ? gg[col % g.seg_n + e] : 1.f);
+            }
+        }
         if constexpr (PREF_R) {
             const Raw8<TR>& res = res_pre[pass * RUNS + it];
 #pragma unroll
@@ -446,9 +460,13 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
     // budget: 2 waves per SIMD).
     switch (kind) {
         case GemmKind::QKV:
-            if constexpr (KS == 1)
+            if constexpr (KS == 1) {
+                if (g.qkn_mask)
+                    return big ? run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 128, 128, 2, 2, D, 32>(g, s)
+                               : run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(g, s);
                 return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, D, 32>(g, s)
                            : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
+            }
             break;
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
             if constexpr (KS == 1) {
@@ -469,7 +487,10 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
             break;
         case GemmKind::KV:
-            if constexpr (KS <= 2) return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
+            if constexpr (KS <= 2) {
+                if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16, KS>(g, s);
+                return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
+            }
             break;
     }
     return hipErrorInvalidValue;
@@ -485,16 +506,45 @@ static int k_groups(GemmKind kind, const GemmArgs& g) {
     return ks;
 }
 
+// fp32 layers: per-head RMS of the stored segments in place (query/key norm),
+// one thread per (row, head).
+__global__ __launch_bounds__(256) void qk_norm_f32_kernel(float* C, int64_t M, int ldc, int seg_n, int head_dim,
+                                                           const float* gain, float eps) {
+    const int heads = seg_n / head_dim;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * heads) return;
+    float* x = C + (idx / heads) * ldc + (idx % heads) * head_dim;
+    const float* gg = gain ? gain + (idx % heads) * head_dim : nullptr;
+    float ss = 0.f;
+    for (int i = 0; i < head_dim; ++i) ss += x[i] * x[i];
+    const float sc = rsqrtf(ss / (float)head_dim + eps);
+    for (int i = 0; i < head_dim; ++i) x[i] *= sc * (gg ? gg[i] : 1.f);
+}
+
+static hipError_t qk_norm_f32(const GemmArgs& g, hipStream_t s) {
+    for (int seg = 0; seg < 3; ++seg) {
+        if (!((g.qkn_mask >> seg) & 1)) continue;
+        const int64_t n = g.M * (g.seg_n / g.head_dim);
+        hipLaunchKernelGGL(qk_norm_f32_kernel, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, s, (float*)g.C[seg],
+                           g.M, (int)g.ldc, g.seg_n, g.head_dim, g.qkn_gain[seg], g.eps);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s) {
     if (dt == RT_F32) {
+        hipError_t e = hipErrorInvalidValue;
         switch (kind) {
-            case GemmKind::QKV: return run_f32<float, EPI_RMS>(g, s);
-            case GemmKind::WO: return run_f32<float, EPI_RESID>(g, s);
-            case GemmKind::W1: return run_f32<float, EPI_RMS | EPI_GELU>(g, s);
-            case GemmKind::W2: return run_f32<float, EPI_RESID>(g, s);
-            case GemmKind::KV: return run_f32<float, EPI_RMS>(g, s);
+            case GemmKind::QKV: e = run_f32<float, EPI_RMS>(g, s); break;
+            case GemmKind::WO: e = run_f32<float, EPI_RESID>(g, s); break;
+            case GemmKind::W1: e = run_f32<float, EPI_RMS | EPI_GELU>(g, s); break;
+            case GemmKind::W2: e = run_f32<float, EPI_RESID>(g, s); break;
+            case GemmKind::KV: e = run_f32<float, EPI_RMS>(g, s); break;
         }
-        return hipErrorInvalidValue;
+        if (e != hipSuccess || !g.qkn_mask) return e;
+        return qk_norm_f32(g, s);
     }
     // K is a multiple of 128 (an even number of 64-wide K tiles); each K group
     // prefetches 4 tiles ahead when its tile count divides by 4, else 2

@@ -47,6 +47,7 @@ enum : int {
     EPI_RMS_PARTS = 8,  // scale rows by 1/rms from n_parts partial sums of squares (rss_in)
     EPI_ROWSS = 16,     // write this tile's partial sum of squares of each stored row (rss_out)
     EPI_COPY = 32,      // also store the result as bf16 into C2
+    EPI_QKNORM = 64,    // RMS-normalise each head_dim-wide head of the segments in qkn_mask
 };
 struct GemmArgs {
     const void* A;      // [M][lda]
@@ -65,6 +66,9 @@ struct GemmArgs {
     int32_t n_parts;
     float* rss_out;       // [M][N / tile width] (EPI_ROWSS)
     void* C2;             // [M][ldc] bf16 (EPI_COPY)
+    int32_t qkn_mask;            // bit s: normalise segment s per head (query/key norm); 0: none
+    int32_t head_dim;            // head width of that norm
+    const float* qkn_gain[3];    // [seg_n] gains per segment (nullptr: ones)
 };
 // Column-tile width of the GEMMs whose epilogue writes row partial sums
 // (the number of partial sums per row is N / this width).

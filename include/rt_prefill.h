@@ -69,6 +69,12 @@ typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
  * pair), so all positions are computed at once with causal attention. The
  * Figure 4 baseline. Excludes RT_FLAG_NAIVE_SCHEDULE. */
 #define RT_FLAG_TRANSFORMER 4u
+/* Query/key norm (translated paper section 2 notation, the separate RMS on
+ * queries and keys after their projections; per head, as in the query/key
+ * normalisation it cites): q, k' and the persistent k are each replaced by
+ * g * x / sqrt(mean(x^2) + rms_eps) over each head's head_dim components,
+ * with gains g_q (queries) and g_k (keys). bf16 layers: head_dim 32 or 64. */
+#define RT_FLAG_QK_NORM 8u
 
 /* Attention shape. softmax_scale (finite, >= 0) multiplies every score <k, q>
  * (the pages' operator has none, i.e. 1.0; workloads use 1/sqrt(head_dim)). */
@@ -93,10 +99,13 @@ typedef struct {
  * W_q, W_k, W_v, W_o: [d][d]; W_1: [F][d]; W_2: [d][F]. The same W_k, W_v
  * form the ephemeral pair (from x_t) and the persistent pair (from z_t).
  * g_attn (RMS gain before Q/K/V) and g_mlp (RMS gain before the MLP) are
- * fp32 [d], or NULL for a vector of ones. */
+ * fp32 [d], or NULL for a vector of ones; so are g_q and g_k, the query/key
+ * norm gains (read only with RT_FLAG_QK_NORM; head h uses entries
+ * h*head_dim .. h*head_dim+head_dim-1). */
 typedef struct {
     const void *w_q, *w_k, *w_v, *w_o, *w_1, *w_2;
     const float *g_attn, *g_mlp;
+    const float *g_q, *g_k;
 } rt_layer_weights;
 
 /*

@@ -121,6 +121,9 @@ class LayerBuffers:
         if gains:
             for n in ("g_attn", "g_mlp"):
                 self.w[n] = torch.from_numpy(np.ascontiguousarray(weights_np[n], dtype=np.float32)).cuda()
+        for n in ("g_q", "g_k"):  # query/key norm gains (fp32), used with RT_FLAG_QK_NORM
+            if weights_np.get(n) is not None:
+                self.w[n] = torch.from_numpy(np.ascontiguousarray(weights_np[n], dtype=np.float32)).cuda()
         td = torch_dtype(dt)
         self.z = torch.empty((N, B, D), dtype=td, device="cuda")
         self.k = torch.empty((N, B, D), dtype=td, device="cuda")

@@ -153,10 +153,20 @@ def test_workspace_bytes_of_the_other_modes(lib):
 
 def test_flags_are_validated(lib):
     W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
-    for flags, text in ((rt.RT_FLAG_NAIVE_SCHEDULE | rt.RT_FLAG_TRANSFORMER, "exclude"), (8, "unknown flags")):
+    for flags, text in ((rt.RT_FLAG_NAIVE_SCHEDULE | rt.RT_FLAG_TRANSFORMER, "exclude"), (64, "unknown flags")):
         with pytest.raises(rt.RtError) as e:
             rt.rt_layer_forward(_layer(flags=flags), W, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
         assert e.value.status == 1 and text in str(e.value)
+    # the bf16 query/key norm works within one 64-column tile: head_dim up to 64
+    wide = _layer(attn=_attn(n_heads=1, head_dim=128), flags=rt.RT_FLAG_QK_NORM)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_forward(wide, W, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+    assert e.value.status == 2 and "head_dim" in str(e.value)
+    assert rt.rt_layer_workspace_bytes(_layer(flags=rt.RT_FLAG_QK_NORM)) == rt.rt_layer_workspace_bytes(_layer())
+    with pytest.raises(rt.RtError) as e:  # gains must be aligned like the other gains
+        rt.rt_layer_forward(_layer(flags=rt.RT_FLAG_QK_NORM), dict(W, g_q=FAKE + 4), FAKE, FAKE, FAKE, FAKE, FAKE,
+                            1 << 30, stream=0)
+    assert "aligned" in str(e.value)
 
 
 def test_decode_rejects_bad_arguments(lib):

@@ -105,6 +105,33 @@ def test_transformer_layer_plan_replays_match_eager():
 
 # ---------------------------------------------------------------- decode against the cache
 
+def _qk_gains(w, seed, d):
+    rng = np.random.default_rng(seed)
+    w = dict(w)
+    w["g_q"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    w["g_k"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    return w
+
+
+@pytest.mark.parametrize("dt,n,b,d,h,f,flags", [
+    ("bf16", 100, 3, 256, 4, 512, 0),                          # head_dim 64, blocked schedule
+    ("bf16", 70, 2, 256, 8, 256, 0),                           # head_dim 32
+    ("f32", 45, 2, 96, 3, 128, 0),
+    ("bf16", 300, 2, 256, 4, 512, 4),                          # Transformer layer (RT_FLAG_TRANSFORMER)
+    ("bf16", 40, 2, 256, 4, 512, 2),                           # naive schedule
+])
+def test_qk_norm_layer_matches_oracle(dt, n, b, d, h, f, flags):
+    """Per-head query/key norm with non-unit gains, on every layer mode."""
+    x = _input(3 * n, n, b, d, dt)
+    w = _qk_gains(_weights(n + 11, d, f, dt), n, d)
+    scale = 1.0 / math.sqrt(d // h)
+    buf = _forward(G.layer_desc(b, n, d, h, f, dt, scale, flags=flags | rt.RT_FLAG_QK_NORM), x, w, dt)
+    ref = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale, round_bf16=(dt == "bf16"), qk_norm=True,
+                               kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER))
+    for name in ("z", "k", "v"):
+        G.parity(G.host(getattr(buf, name)), ref[name], dt, f"qk_norm[{flags}].{name}")
+
+
 def _decode_case(dt, n_past, steps, b, d, h, f, flags=0, seed=0, scale=None):
     """Prefill positions 1..n_past with rt_layer_forward into caches of capacity
     n_past+steps, then decode positions n_past+1..n_past+steps one by one.
@@ -114,12 +141,14 @@ def _decode_case(dt, n_past, steps, b, d, h, f, flags=0, seed=0, scale=None):
     n = n_past + steps
     x = _input(seed + n, n, b, d, dt)
     w = _weights(seed + n + 1, d, f, dt)
+    if flags & rt.RT_FLAG_QK_NORM:
+        w = _qk_gains(w, seed + n + 2, d)
     scale = 1.0 / math.sqrt(d // h) if scale is None else scale
     td = G.torch_dtype(dt)
     kc = torch.full((n, b, d), float("nan"), dtype=td, device="cuda")
     vc = torch.full((n, b, d), float("nan"), dtype=td, device="cuda")
     x_dev = G.dev(x, dt)
-    W = {k: G.dev(v, dt) for k, v in w.items()}
+    W = {k: G.dev(v, "f32" if k.startswith("g_") else dt) for k, v in w.items()}  # gains are fp32
     if n_past:
         pre = G.layer_desc(b, n_past, d, h, f, dt, scale, flags=flags)
         z_pre = torch.empty((n_past, b, d), dtype=td, device="cuda")
@@ -133,7 +162,8 @@ def _decode_case(dt, n_past, steps, b, d, h, f, flags=0, seed=0, scale=None):
         rt.rt_layer_decode_step(desc, W, n_past + i, x_dev[n_past + i], z[i], kc, vc, ws)
     torch.cuda.synchronize()
     ref = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale, round_bf16=(dt == "bf16"),
-                               kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER))
+                               kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER),
+                               qk_norm=bool(flags & rt.RT_FLAG_QK_NORM))
     return G.host(z), G.host(kc), G.host(vc), ref
 
 
@@ -153,6 +183,14 @@ def test_decode_steps_match_oracle(dt, n_past, h, scale):
     G.parity(kc, ref["k"], dt, f"decode.k_cache (n_past={n_past})")
     G.parity(vc, ref["v"], dt, f"decode.v_cache (n_past={n_past})")
     assert kc.shape[0] == n
+
+
+def test_qk_norm_decode_steps_match_oracle():
+    steps, b, d, h, f, n_past = 3, 2, 256, 4, 512, 45
+    z, kc, vc, ref = _decode_case("bf16", n_past, steps, b, d, h, f, flags=rt.RT_FLAG_QK_NORM, seed=9)
+    G.parity(z, ref["z"][n_past:], "bf16", "qk_norm decode.z")
+    G.parity(kc, ref["k"], "bf16", "qk_norm decode.k_cache")
+    G.parity(vc, ref["v"], "bf16", "qk_norm decode.v_cache")
 
 
 @pytest.mark.parametrize("n_past", [0, 50])
