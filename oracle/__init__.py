@@ -64,6 +64,8 @@ def lib():
             ctypes.c_int, ctypes.POINTER(ctypes.c_int), _dp]
         L.rto_layer_forward.restype = ctypes.c_int
         L.rto_layer_forward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Weights), _fp, ctypes.POINTER(_Out)]
+        L.rto_attention_backward.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double] + [_fp] * 6 + [_dp] * 5
+        L.rto_attention_backward.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -117,6 +119,23 @@ def attention(q, k_eph, v_eph, k, v, softmax_scale: float) -> np.ndarray:
     if st != 0:
         raise RuntimeError(f"rto_attention failed with status {st}")
     return out
+
+
+def attention_backward(q, k_eph, v_eph, k, v, a_bar, softmax_scale: float) -> dict:
+    """Gradient of the naive RT attention map for the output adjoint a_bar = dL/da
+    (all [N][R][H][dh]): returns float64 q, k_eph, v_eph, k, v gradients by name."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    arrs = [_f32(t) for t in (q, k_eph, v_eph, k, v, a_bar)]
+    for a, _ in arrs:
+        if a.shape != q.shape:
+            raise ValueError("all attention tensors must share one shape")
+    N, R, H, dh = q.shape
+    outs = {n: np.empty(q.shape, dtype=np.float64) for n in ("q", "k_eph", "v_eph", "k", "v")}
+    st = lib().rto_attention_backward(N, R, H, dh, softmax_scale, *[p for _, p in arrs],
+                                      *[outs[n].ctypes.data_as(_dp) for n in ("q", "k_eph", "v_eph", "k", "v")])
+    if st != 0:
+        raise RuntimeError(f"rto_attention_backward failed with status {st}")
+    return outs
 
 
 def attention_at(q, k_eph, v_eph, k, v, softmax_scale: float, positions) -> np.ndarray:

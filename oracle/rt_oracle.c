@@ -186,6 +186,98 @@ int rto_attention(int n_pos, int n_rows, int n_heads, int head_dim, double sigma
 }
 
 /*
+ * Gradient of the RT attention map (the naive definition above) for a given
+ * output adjoint a_bar = dL/da, all [n_pos][n_rows][n_heads][head_dim]. The
+ * pages state only that the backward can be batched outside the position
+ * loop; this is the chain rule written out for one query t:
+ *   s_i = sigma <q, k_i> (i < t),  s_e = sigma <q, k'_t>,  p = softmax(s)
+ *   a   = sum_i p_i v_i + p_e v'_t
+ *   D   = <a_bar, a>,  dp_i = <a_bar, v_i>,  ds_i = p_i (dp_i - D)   (same for e)
+ *   v_bar_i += p_i a_bar,   v'_bar_t = p_e a_bar
+ *   k_bar_i += sigma ds_i q,  k'_bar_t = sigma ds_e q,
+ *   q_bar_t  = sigma (sum_i ds_i k_i + ds_e k'_t).
+ * Outputs are fp64 and fully written.
+ */
+int rto_attention_backward(int n_pos, int n_rows, int n_heads, int head_dim, double sigma,
+                           const float* q, const float* k_eph, const float* v_eph,
+                           const float* k, const float* v, const float* a_bar,
+                           double* q_bar, double* k_eph_bar, double* v_eph_bar, double* k_bar, double* v_bar) {
+    if (n_pos < 0 || n_rows < 0 || n_heads <= 0 || head_dim <= 0 || head_dim > 512) return RTO_BAD_ARG;
+    if (!q || !k_eph || !v_eph || !k || !v || !a_bar || !q_bar || !k_eph_bar || !v_eph_bar || !k_bar || !v_bar)
+        return RTO_BAD_ARG;
+    const int d = n_heads * head_dim, dh = head_dim;
+    const size_t stride = (size_t)n_rows * d;
+    int status = RTO_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int pr = 0; pr < n_rows * n_heads; ++pr) {
+        const int r = pr / n_heads, h = pr % n_heads;
+        const size_t base = (size_t)r * d + (size_t)h * dh;
+        double* p = malloc(sizeof(double) * (size_t)(n_pos + 1));
+        if (!p) {
+#pragma omp atomic write
+            status = RTO_NO_MEMORY;
+            continue;
+        }
+        for (int t = 0; t < n_pos; ++t)
+            for (int e = 0; e < dh; ++e) {
+                k_bar[(size_t)t * stride + base + e] = 0.0;
+                v_bar[(size_t)t * stride + base + e] = 0.0;
+            }
+        for (int t = 0; t < n_pos; ++t) {
+            const size_t ot = (size_t)t * stride + base;
+            const float *qt = q + ot, *ket = k_eph + ot, *vet = v_eph + ot, *abt = a_bar + ot;
+            /* probabilities over persistent pairs 0..t-1 (p[0..t-1]) and the ephemeral pair (p[t]) */
+            double mx = -INFINITY;
+            for (int i = 0; i <= t; ++i) {
+                const float* ki = i < t ? k + (size_t)i * stride + base : ket;
+                double sd = 0.0;
+                for (int e = 0; e < dh; ++e) sd += (double)qt[e] * ki[e];
+                p[i] = sigma * sd;
+                if (p[i] > mx) mx = p[i];
+            }
+            double den = 0.0;
+            for (int i = 0; i <= t; ++i) {
+                p[i] = exp(p[i] - mx);
+                den += p[i];
+            }
+            for (int i = 0; i <= t; ++i) p[i] /= den;
+            /* D = <a_bar, a> with a = sum_i p_i v_i */
+            double D = 0.0;
+            for (int i = 0; i <= t; ++i) {
+                const float* vi = i < t ? v + (size_t)i * stride + base : vet;
+                double dpi = 0.0;
+                for (int e = 0; e < dh; ++e) dpi += (double)abt[e] * vi[e];
+                D += p[i] * dpi;
+            }
+            double* qb = q_bar + ot;
+            for (int e = 0; e < dh; ++e) qb[e] = 0.0;
+            for (int i = 0; i <= t; ++i) {
+                const int eph = i == t;
+                const float* ki = eph ? ket : k + (size_t)i * stride + base;
+                const float* vi = eph ? vet : v + (size_t)i * stride + base;
+                double* kb = eph ? k_eph_bar + ot : k_bar + (size_t)i * stride + base;
+                double* vb = eph ? v_eph_bar + ot : v_bar + (size_t)i * stride + base;
+                double dpi = 0.0;
+                for (int e = 0; e < dh; ++e) dpi += (double)abt[e] * vi[e];
+                const double ds = p[i] * (dpi - D);
+                for (int e = 0; e < dh; ++e) {
+                    if (eph) {
+                        kb[e] = sigma * ds * qt[e];
+                        vb[e] = p[i] * abt[e];
+                    } else {
+                        kb[e] += sigma * ds * qt[e];
+                        vb[e] += p[i] * abt[e];
+                    }
+                    qb[e] += sigma * ds * ki[e];
+                }
+            }
+        }
+        free(p);
+    }
+    return status;
+}
+
+/*
  * The same attention for selected positions only: a_sel[i] is the output of
  * position sel[i] (1-based), [n_sel][n_rows][n_heads][head_dim]. Position t
  * reads the persistent pairs 1..t-1 and its own ephemeral pair, so any
