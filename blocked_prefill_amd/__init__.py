@@ -14,7 +14,8 @@ __all__ = [
     "RT_F32", "RT_BF16", "RtError", "AttnDesc", "LayerDesc", "LayerWeights", "load", "library_path",
     "rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes",
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
-    "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_last_error", "EXPORTED",
+    "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
+    "rt_last_error", "EXPORTED",
     "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
 ]
 
@@ -31,7 +32,8 @@ library_path = os.path.join(_HERE, "librt_prefill.so")
 # every symbol include/rt_prefill.h declares
 EXPORTED = ["rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes", "rt_layer_forward",
             "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
-            "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_last_error"]
+            "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
+            "rt_last_error"]
 
 
 class RtError(RuntimeError):
@@ -76,6 +78,8 @@ def load():
             "rt_layer_plan_create": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _vp, _vp, _vp, _vp,
                                      _vp, ctypes.c_size_t, ctypes.POINTER(_vp)],
             "rt_layer_plan_launch": [_vp, _vp],
+            "rt_attn_forward": [ctypes.POINTER(AttnDesc)] + [_vp] * 11,
+            "rt_attn_backward": [ctypes.POINTER(AttnDesc)] + [_vp] * 15,
             "rt_layer_decode_step": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _i32, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, _vp],
             "rt_schedule_step": [_i32, _i32] + [ctypes.POINTER(_i32)] * 4,
@@ -142,6 +146,17 @@ def rt_finalize_step(desc: AttnDesc, t: int, q, k_eph, v_eph, m, l, o, a_t, stre
 def rt_update_finalize_step(desc: AttnDesc, t: int, q, k_eph, v_eph, k, v, m, l, o, a_next, stream=None):
     _check(load().rt_update_finalize_step(ctypes.byref(desc), t, _ptr(q), _ptr(k_eph), _ptr(v_eph), _ptr(k), _ptr(v),
                                           _ptr(m), _ptr(l), _ptr(o), _ptr(a_next), _stream(stream)))
+
+
+def rt_attn_forward(desc: AttnDesc, q, k_eph, v_eph, k, v, a, lse, m, l, o, stream=None):
+    _check(load().rt_attn_forward(ctypes.byref(desc), *[_ptr(t) for t in (q, k_eph, v_eph, k, v, a, lse, m, l, o)],
+                                  _stream(stream)))
+
+
+def rt_attn_backward(desc: AttnDesc, q, k_eph, v_eph, k, v, a, lse, a_bar, q_bar, k_eph_bar, v_eph_bar, k_bar,
+                     v_bar, delta, stream=None):
+    _check(load().rt_attn_backward(ctypes.byref(desc), *[_ptr(t) for t in (
+        q, k_eph, v_eph, k, v, a, lse, a_bar, q_bar, k_eph_bar, v_eph_bar, k_bar, v_bar, delta)], _stream(stream)))
 
 
 def rt_layer_workspace_bytes(desc: LayerDesc) -> int:

@@ -460,6 +460,72 @@ rt_status rt_update_finalize_step(const rt_attn_desc* desc, int32_t t, const voi
     return e == hipSuccess ? RT_OK : hip_fail(e, "rt_update_finalize_step launch");
 }
 
+rt_status rt_attn_forward(const rt_attn_desc* desc, const void* q, const void* k_eph, const void* v_eph,
+                          const void* k, const void* v, void* a, float* lse, float* m, float* l, float* o,
+                          rt_stream_t stream) {
+    RT_TRY(check_attn(desc));
+    const void* ps[] = {q, k_eph, v_eph, k, v, a, lse, m, l, o};
+    const char* names[] = {"q", "k_eph", "v_eph", "k", "v", "a", "lse", "m", "l", "o"};
+    for (int i = 0; i < 10; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i]) && i != 6 && i != 7 && i != 8)
+            return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (((uintptr_t)lse & 3u) || ((uintptr_t)m & 3u) || ((uintptr_t)l & 3u))
+        return fail(RT_ERR_INVALID_ARG, "lse, m and l must be 4-byte aligned");
+    const int32_t N = desc->seq_len;
+    const size_t slab = (size_t)desc->batch * desc->n_heads * desc->head_dim * elem_bytes(desc->dtype);
+    hipStream_t s = (hipStream_t)stream;
+    rt::UpdateArgs u{};
+    u.q = q; u.k = k; u.v = v; u.k_eph = k_eph; u.v_eph = v_eph; u.m = m; u.l = l; u.o = o; u.lse = lse;
+    u.P = (int64_t)desc->batch * desc->n_heads;
+    u.sigma2 = desc->softmax_scale * rt::kLog2eHost;
+    // position 1, then the fused steps t = 1..N-1 (each finishing position t+1)
+    u.a_out = a; u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
+    hipError_t e = rt::launch_update(desc->dtype, desc->head_dim, u, s);
+    for (int32_t t = 1; t < N && e == hipSuccess; ++t) {
+        const int32_t b = block_of(t);
+        u.a_out = (char*)a + (size_t)t * slab;
+        u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
+        u.init = (b == t); u.fin = 1;
+        e = rt::launch_update(desc->dtype, desc->head_dim, u, s);
+    }
+    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_attn_forward launch");
+}
+
+rt_status rt_attn_backward(const rt_attn_desc* desc, const void* q, const void* k_eph, const void* v_eph,
+                           const void* k, const void* v, const void* a, const float* lse, const float* a_bar,
+                           float* q_bar, float* k_eph_bar, float* v_eph_bar, float* k_bar, float* v_bar,
+                           float* delta, rt_stream_t stream) {
+    RT_TRY(check_attn(desc));
+    const void* ps[] = {q, k_eph, v_eph, k, v, a, lse, a_bar, q_bar, k_eph_bar, v_eph_bar, k_bar, v_bar, delta};
+    const char* names[] = {"q", "k_eph", "v_eph", "k", "v", "a", "lse", "a_bar", "q_bar", "k_eph_bar",
+                           "v_eph_bar", "k_bar", "v_bar", "delta"};
+    for (int i = 0; i < 14; ++i) {
+        if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+        if (!aligned16(ps[i]) && i != 6 && i != 13)
+            return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (((uintptr_t)lse & 3u) || ((uintptr_t)delta & 3u))
+        return fail(RT_ERR_INVALID_ARG, "lse and delta must be 4-byte aligned");
+    const int32_t N = desc->seq_len, dh = desc->head_dim;
+    hipStream_t s = (hipStream_t)stream;
+    rt::BackwardArgs bw{};
+    bw.q = q; bw.k_eph = k_eph; bw.v_eph = v_eph; bw.k = k; bw.v = v; bw.a = a; bw.lse = lse; bw.a_bar = a_bar;
+    bw.q_bar = q_bar; bw.k_eph_bar = k_eph_bar; bw.v_eph_bar = v_eph_bar; bw.k_bar = k_bar; bw.v_bar = v_bar;
+    bw.delta = delta; bw.P = (int64_t)desc->batch * desc->n_heads; bw.n_pos = N;
+    bw.sigma = desc->softmax_scale; bw.sigma2 = desc->softmax_scale * rt::kLog2eHost;
+    hipError_t e = rt::launch_backward_prep(desc->dtype, dh, bw, s);
+    // the forward's steps in order: step t's rectangle sets key row t (its first visit)
+    for (int32_t t = 1; t < N && e == hipSuccess; ++t) {
+        const int32_t b = block_of(t);
+        e = rt::launch_backward_step(desc->dtype, dh, bw, t - b, b, t, (b < N - t) ? b : N - t, s);
+    }
+    // the last position's pair is read by no query
+    if (e == hipSuccess) e = rt::launch_backward_zero_rows(dh, bw, N - 1, 1, s);
+    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_attn_backward launch");
+}
+
 size_t rt_layer_workspace_bytes(const rt_layer_desc* desc) {
     if (check_layer(desc) != RT_OK) return 0;
     return layout_of(desc, mode_of(desc)).total;

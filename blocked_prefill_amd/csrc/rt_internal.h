@@ -31,12 +31,36 @@ struct UpdateArgs {
     float sigma2;       // softmax_scale * log2(e)
     int32_t init;       // state rows are initialised, not read (first touch)
     int32_t fin;        // row q0 is finished into a_out and its state is not written
+    float* lse;         // [N][P] (nullable): base-2 log-sum-exp of the finished row, m + log2(l)
 };
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
 // Plain causal attention over nq positions: query row i attends key/value rows
 // 0..i of k/v and is written to row i of a_out ([nq][P][dh]); m/l/o unused.
 hipError_t launch_causal_attention(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
+
+// Attention backward of the blocked schedule (see backward.hip). Tensors as
+// in UpdateArgs; adjoints and outputs fp32 [N][P][dh], lse/delta fp32 [N][P].
+struct BackwardArgs {
+    const void *q, *k_eph, *v_eph, *k, *v, *a;  // dtype
+    const float* lse;                           // base-2 log-sum-exp of every query
+    const float* a_bar;                         // output adjoint
+    float *q_bar, *k_eph_bar, *v_eph_bar, *k_bar, *v_bar;
+    float* delta;                               // <a_bar, a> per query (written by the first pass)
+    int64_t P;
+    int32_t n_pos;
+    float sigma;                                // softmax_scale (natural units)
+    float sigma2;                               // softmax_scale * log2(e)
+};
+// Per-query pass over all positions: delta, the ephemeral pair's gradients, q_bar's ephemeral term.
+hipError_t launch_backward_prep(rt_dtype dt, int head_dim, const BackwardArgs& b, hipStream_t s);
+// Step t of the blocked schedule, reversed: the block of keys (kv0, kv0+nkv] against the queries
+// (q0, q0+nq]; k_bar/v_bar rows of the block accumulate (row kv0+nkv-1, first touched here, is set),
+// q_bar rows of the queries accumulate.
+hipError_t launch_backward_step(rt_dtype dt, int head_dim, const BackwardArgs& b, int32_t kv0, int32_t nkv,
+                                int32_t q0, int32_t nq, hipStream_t s);
+// Zero rows [row0, row0 + rows) of k_bar and v_bar (pairs no query reads).
+hipError_t launch_backward_zero_rows(int head_dim, const BackwardArgs& b, int32_t row0, int32_t rows, hipStream_t s);
 
 // C[M][N] = epilogue(A[M][K] * W^T), W given as up to 3 column segments of
 // seg_n rows each ([seg_n][K] row-major), outputs likewise split.

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) out[e] = (ob[e] * c + pe * ve[e]) * inv;
         store8((T*)a.a_out + off, out);
+        if (a.lse && lane == 0) a.lse[j * a.P + p] = mn + log2f(lb);  // saved for the backward
     } else {
         if (lane == 0) {
             a.m[sidx] = mb;
@@ -192,6 +193,7 @@ __global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) ob[e] *= inv;
             store8((T*)a.a_out + off, ob);
+            if (a.lse && lane == 0) a.lse[sidx] = mb + log2f(lb);  // saved for the backward
         } else {
             if (lane == 0) {
                 a.m[sidx] = mb;
@@ -467,6 +469,7 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
         const float m_new = fmaxf(m_run, d);
         const float c = fast_exp2(m_run - m_new), pe = fast_exp2(d - m_new);
         const float inv = 1.0f / (l_run * c + pe);
+        if (a.lse && g == 0) a.lse[j * a.P + pair] = m_new + log2f(l_run * c + pe);  // saved for the backward
         const bf16* vp = (const bf16*)a.v_eph + j * slab + pair * DH;
         bf16* out = (bf16*)a.a_out + pair * DH;
 #pragma unroll

@@ -161,6 +161,43 @@ rt_status rt_update_finalize_step(const rt_attn_desc* desc, int32_t t,
                                   float* m, float* l, float* o, void* a_next, rt_stream_t stream);
 
 /*
+ * rt_attn_forward -- the blocked-schedule attention of a whole sequence with
+ * every pair known up front (the update and finalize steps above, in order),
+ * saving what its backward needs:
+ *   q, k_eph, v_eph, k, v [N][B][H][dh] (dtype), read
+ *   a   [N][B][H][dh] (dtype): attention outputs, written
+ *   lse [N][B][H] fp32: each query's base-2 log-sum-exp, m + log2(l) in the
+ *       state's units (s = softmax_scale*log2(e)*<k,q>), written
+ *   m, l [N][B][H], o [N][B][H][dh] fp32: the online-softmax state (scratch)
+ */
+rt_status rt_attn_forward(const rt_attn_desc* desc, const void* q, const void* k_eph, const void* v_eph,
+                          const void* k, const void* v, void* a, float* lse, float* m, float* l, float* o,
+                          rt_stream_t stream);
+
+/*
+ * rt_attn_backward -- gradient of that attention for an output adjoint
+ * a_bar = dL/da. The pages say only that the RT backward can be batched
+ * outside the position loop (reading note, summary section 5.3; the
+ * translated paper's backward section is missing); the gradient is the chain
+ * rule through each query's softmax (D_t = <a_bar_t, a_t>, ds_i = p_i
+ * (<a_bar_t, v_i> - D_t); v_bar_i += p_i a_bar_t, k_bar_i += sigma ds_i q_t,
+ * q_bar_t += sigma ds_i k_i), applied in the forward's blocked rectangles
+ * (step t: keys t-b+1..t against queries t+1..t+b) with probabilities
+ * recomputed from the saved lse, plus one per-query pass for the ephemeral
+ * pair.
+ *   q, k_eph, v_eph, k, v, a [N][B][H][dh] (dtype), lse [N][B][H] fp32: as
+ *       used and saved by rt_attn_forward
+ *   a_bar [N][B][H][dh] fp32, read
+ *   q_bar, k_eph_bar, v_eph_bar, k_bar, v_bar [N][B][H][dh] fp32: written
+ *       (every element; the caller clears nothing)
+ *   delta [N][B][H] fp32: scratch
+ */
+rt_status rt_attn_backward(const rt_attn_desc* desc, const void* q, const void* k_eph, const void* v_eph,
+                           const void* k, const void* v, const void* a, const float* lse, const float* a_bar,
+                           float* q_bar, float* k_eph_bar, float* v_eph_bar, float* k_bar, float* v_bar,
+                           float* delta, rt_stream_t stream);
+
+/*
  * rt_layer_workspace_bytes -- device workspace that rt_layer_forward and
  * rt_layer_plan_create need for this shape, or 0 for an invalid descriptor.
  */

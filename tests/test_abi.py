@@ -102,6 +102,23 @@ def test_update_at_last_position_is_a_noop(lib):
     rt.rt_blocked_attn_update(_attn(seq_len=16), 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
 
 
+def test_attention_forward_and_backward_reject_bad_arguments(lib):
+    d = _attn()
+    args = [FAKE] * 10
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_attn_forward(d, *args[:6], None, *args[7:], stream=0)
+    assert "lse is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_attn_forward(d, FAKE + 8, *args[1:], stream=0)
+    assert "aligned" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_attn_backward(d, *([FAKE] * 13), None, stream=0)
+    assert "delta is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_attn_backward(_attn(head_dim=48), *([FAKE] * 14), stream=0)
+    assert e.value.status == 2
+
+
 def test_finalize_rejects_bad_arguments(lib):
     d = _attn()
     with pytest.raises(rt.RtError):
