@@ -229,6 +229,62 @@ def sweep(args):
     print(json.dumps(out))
 
 
+def backward(args):
+    """Attention backward of the blocked schedule at the layer's attention shape
+    (B=512, 16 heads x 64, N=2048, bf16 inputs, fp32 gradients): rt_attn_forward
+    (saving the log-sum-exp) once, then rt_attn_backward timed (mean of 3 after 1).
+    Algorithmic work: every causal (key, query) pair once, 10*dh flops (scores and
+    value products recomputed, then the q, k, v gradient products), plus the
+    per-query pass."""
+    import torch
+
+    import blocked_prefill_amd as rt
+    import rt_inputs
+    rt.load()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    B, H, dh, N = 512, 16, 64, 2048
+    wl = rt_inputs.Workload("attn_b512_n2048", B, N, H * dh, H, dh, 0, 0, "bf16", 1003, update_only=True)
+    t = rt_inputs.attn_inputs(wl)
+    bf = {k: torch.from_numpy(t[k]).to(torch.bfloat16).to(dev) for k in ("q", "k_eph", "v_eph", "k", "v")}
+    del t
+    f32 = dict(dtype=torch.float32, device=dev)
+    desc = rt.AttnDesc(batch=B, seq_len=N, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=0.125)
+    a = torch.empty_like(bf["q"])
+    lse, m, l = (torch.empty((N, B, H), **f32) for _ in range(3))
+    o = torch.empty((N, B, H, dh), **f32)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rt.rt_attn_forward(desc, bf["q"], bf["k_eph"], bf["v_eph"], bf["k"], bf["v"], a, lse, m, l, o, stream=stream)
+    e0.record(stream)
+    rt.rt_attn_forward(desc, bf["q"], bf["k_eph"], bf["v_eph"], bf["k"], bf["v"], a, lse, m, l, o, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1)
+    del m, l, o
+    a_bar = torch.randn((N, B, H, dh), generator=torch.Generator(device=dev).manual_seed(5), **f32)
+    outs = [torch.empty((N, B, H, dh), **f32) for _ in range(5)]
+    delta = torch.empty((N, B, H), **f32)
+    call = lambda: rt.rt_attn_backward(desc, bf["q"], bf["k_eph"], bf["v_eph"], bf["k"], bf["v"], a, lse, a_bar,
+                                       *outs, delta, stream=stream)
+    call()
+    torch.cuda.synchronize()
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    P = B * H
+    flops = 10.0 * dh * P * (N * (N - 1) / 2) + 12.0 * dh * P * N
+    print(json.dumps({"backward": "blocked-schedule attention backward, B=512, 16x64 heads, N=2048, bf16 inputs",
+                      "ms": round(ms, 3), "forward_with_lse_ms": round(fwd_ms, 3),
+                      "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+                      "alg_TFLOP": round(flops / 1e12, 3), "TFLOP_s": round(flops / (ms * 1e-3) / 1e12, 2),
+                      "bound": "mfma", "peak_TFLOP_s": 2500.0,
+                      "frac": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}))
+
+
 def decode(args):
     """One decode step (a new position per sequence against the persistent KV
     cache) of the B=512, d=1024 layer after a 2048-position prefill: mean of
@@ -295,6 +351,8 @@ def main():
                          "Transformer (log-log slopes)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter passes over --counters (no GPU needed)")
+    ap.add_argument("--backward", action="store_true",
+                    help="attention backward of the blocked schedule at B=512, 16x64 heads, N=2048")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
     args = ap.parse_args()
@@ -321,6 +379,8 @@ def main():
         return sweep(args)
     if args.decode:
         return decode(args)
+    if args.backward:
+        return backward(args)
     wl = rt_inputs.WORKLOADS[args.workload]
     N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
     scale = 1.0 / math.sqrt(dh)

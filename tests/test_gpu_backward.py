@@ -66,6 +66,7 @@ def _check(got, want, dt, what):
     rel = float(np.linalg.norm(err) / max(np.linalg.norm(want), 1e-300))
     assert np.all(np.isfinite(got)), what
     assert rel <= BAR[dt], f"{what}: rel-L2 {rel:.3g} (max-abs {np.abs(err).max():.3g}) over {BAR[dt]}"
+    print(f"{what}: rel-L2 {rel:.3g}")
     return rel
 
 
