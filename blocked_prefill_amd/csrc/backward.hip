@@ -70,12 +70,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardArgs b) {
 // the step's queries. The block's last row is first touched by this step (a
 // row's first step is its own position), so it is set; the others accumulate.
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BackwardArgs b, int32_t kv0, int32_t nkv, int32_t q0, int32_t nq) {
+__device__ __forceinline__ void bwd_kv_item(const BackwardArgs& b, int64_t item, int lane, int32_t kv0, int32_t nkv,
+                                            int32_t q0, int32_t nq) {
     constexpr int G = DH / 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t item = gid / G;
-    const int lane = (int)(gid % G);
-    if (item >= (int64_t)nkv * b.P) return;
     const int64_t i = kv0 + item / b.P, p = item % b.P;
     const int64_t slab = b.P * DH, off = p * DH + lane * 8;
     float k[8], v[8];
@@ -123,12 +120,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BackwardArgs b, int32_t kv0
 // Step rectangle, query side: one 8-lane group per (query row j, pair p) loops
 // over the step's keys and adds its term to q_bar_j.
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void bwd_q_kernel(BackwardArgs b, int32_t kv0, int32_t nkv, int32_t q0, int32_t nq) {
+__device__ __forceinline__ void bwd_q_item(const BackwardArgs& b, int64_t item, int lane, int32_t kv0, int32_t nkv,
+                                           int32_t q0, int32_t nq) {
     constexpr int G = DH / 8;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t item = gid / G;
-    const int lane = (int)(gid % G);
-    if (item >= (int64_t)nq * b.P) return;
     const int64_t j = q0 + item / b.P, p = item % b.P;
     const int64_t slab = b.P * DH, off = p * DH + lane * 8;
     float q[8], ab[8];
@@ -159,6 +153,23 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BackwardArgs b, int32_t kv0,
 #pragma unroll
     for (int e = 0; e < 8; ++e) qb[e] += qo[e];
     store8(qr, qb);
+}
+
+// Both sides of a step in one launch: items [0, nkv*P) are keys, the rest
+// queries. A wave may hold both kinds, but each G-lane group is one item, so
+// the group sums' shuffles never cross from one kind to the other.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void bwd_step_kernel(BackwardArgs b, int32_t kv0, int32_t nkv, int32_t q0,
+                                                        int32_t nq) {
+    constexpr int G = DH / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t item = gid / G;
+    const int lane = (int)(gid % G);
+    const int64_t nk_items = (int64_t)nkv * b.P;
+    if (item < nk_items)
+        bwd_kv_item<T, DH>(b, item, lane, kv0, nkv, q0, nq);
+    else if (item < nk_items + (int64_t)nq * b.P)
+        bwd_q_item<T, DH>(b, item - nk_items, lane, kv0, nkv, q0, nq);
 }
 
 // ---------------------------------------------------------------- MFMA (bf16, head_dim 64, blocks >= 32)
@@ -459,10 +470,8 @@ static hipError_t prep_typed(int dh, const BackwardArgs& b, hipStream_t s) {
 
 template <typename T, int DH>
 static hipError_t step_dh(const BackwardArgs& b, int32_t kv0, int32_t nkv, int32_t q0, int32_t nq, hipStream_t s) {
-    hipLaunchKernelGGL((bwd_kv_kernel<T, DH>), grid_for((int64_t)nkv * b.P, DH), dim3(256), 0, s, b, kv0, nkv, q0, nq);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_q_kernel<T, DH>), grid_for((int64_t)nq * b.P, DH), dim3(256), 0, s, b, kv0, nkv, q0, nq);
+    hipLaunchKernelGGL((bwd_step_kernel<T, DH>), grid_for((int64_t)(nkv + nq) * b.P, DH), dim3(256), 0, s, b, kv0,
+                       nkv, q0, nq);
     return hipGetLastError();
 }
 

@@ -6,7 +6,9 @@ Bars on every gradient, relative L2 against the oracle's fp64 gradient:
 fp32 inputs 1e-5 (fp32 arithmetic over sums of up to N terms); bf16 inputs
 5e-3: the stored attention output a is bf16 (as the forward keeps it), and
 delta = <a_bar, a> enters every score's gradient, so a's half-ulp rounding
-(2^-9 relative) reaches the gradients at that level.
+(2^-9 relative) reaches the gradients at that level; the MFMA rectangles
+(blocks of 32 pairs and more) also round a_bar, the probabilities and the
+score gradients to bf16 as product operands, each again 2^-9 relative.
 """
 import math
 
