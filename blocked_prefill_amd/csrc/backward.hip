@@ -233,7 +233,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
     const bf16* vb = (const bf16*)b.v + (int64_t)kv0 * slab + pair * DH;
     const int krow = swap23(ql);
     for (int kt0 = 0; kt0 < nkv; kt0 += KT) {
-        const int rows = min(nkv - kt0, KT);  // 32 or 64 (nkv is a multiple of 32)
+        const int rows = min(nkv - kt0, KT);  // the last tile may be short (a block of 16)
         lds_fence_barrier_bwd();
         for (int c = tid; c < KT * 8; c += NT) {
             const int r = min(c >> 3, rows - 1), ch = (c & 7) * 8;
@@ -261,12 +261,14 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, aop[i], dp, 0, 0, 0);
             }
             bf16x8 s0, s1;  // dS^T in the B layout: keys 8g.. (e < 8) and 16+8g.. (e >= 8)
+            // keys past a short block's end repeat its last row: their score gradients are zeroed
+            const int live = rows - c32 - 8 * g;  // keys 8g + e (e < live) and 16 + 8g + e (e < live - 16) exist
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float pa = fast_exp2(__builtin_fmaf(st[e], sigma2, -lse));
                 const float pb = fast_exp2(__builtin_fmaf(st[e + 8], sigma2, -lse));
-                s0[e] = (bf16)(pa * (dp[e] - dd));
-                s1[e] = (bf16)(pb * (dp[e + 8] - dd));
+                s0[e] = (bf16)(e < live ? pa * (dp[e] - dd) : 0.f);
+                s1[e] = (bf16)(e + 16 < live ? pb * (dp[e + 8] - dd) : 0.f);
             }
             const bf16* k_lo = &Kt[ql * STR + c32 + 8 * g];
             const bf16* k_hi = &Kt[(32 + ql) * STR + c32 + 8 * g];
@@ -506,9 +508,10 @@ static hipError_t step_mfma(const BackwardArgs& b, int32_t kv0, int32_t nkv, int
 hipError_t launch_backward_step(rt_dtype dt, int head_dim, const BackwardArgs& b, int32_t kv0, int32_t nkv,
                                 int32_t q0, int32_t nq, hipStream_t s) {
     if (nkv <= 0 || nq <= 0) return hipSuccess;
-    // blocks of 32 pairs and more (a multiple of 32 in the blocked schedule): MFMA rectangles
+    // blocks of 32 pairs and more (powers of two in the blocked schedule): MFMA rectangles
+    // (blocks of 16 measured no faster there than on the SIMT kernel)
     if (dt == RT_BF16 && head_dim == 64 && nkv >= 32 && nkv % 32 == 0) {
-        const int w = nkv >= 128 ? 4 : nkv / 32;  // waves per workgroup on the key side (1, 2 or 4)
+        const int w = nkv >= 128 ? 4 : (nkv >= 64 ? 2 : 1);  // waves per workgroup on the key side
         return w == 4 ? step_mfma<4>(b, kv0, nkv, q0, nq, s)
                       : (w == 2 ? step_mfma<2>(b, kv0, nkv, q0, nq, s) : step_mfma<1>(b, kv0, nkv, q0, nq, s));
     }
