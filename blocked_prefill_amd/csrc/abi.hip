@@ -222,9 +222,12 @@ rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const P
 // Everything after the attention, for `rows` rows:
 //   h = x + rho W_o a;  z = h + rho W_2 GELU(W_1 RMS_mlp(h));
 //   and, when kt is not NULL, the persistent pair k|v = W_{k,v} RMS_attn(z).
+// fuse (bf16, head_dim 64): a blocked step of 1, 2 or 4 pairs ending at this
+// position, run by the K/V projection's own workgroups once they have stored
+// the pair (one launch fewer on the position's critical path).
 rt_status enqueue_tail(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, char* base,
                        const Layout& L, int64_t rows, const void* a, const void* x, void* z, void* kt, void* vt,
-                       Launcher& run) {
+                       Launcher& run, const rt::UpdateArgs* fuse = nullptr) {
     using namespace rt;
     const rt_dtype dt = d->attn.dtype;
     const int32_t D = d->d_model, F = d->d_ff;
@@ -261,6 +264,10 @@ rt_status enqueue_tail(const rt_layer_desc* d, const rt_layer_weights* w, const 
     gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
     if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
     if (d->flags & RT_FLAG_QK_NORM) { gk.qkn_mask = 1; gk.head_dim = d->attn.head_dim; gk.qkn_gain[0] = w->g_k; }
+    if (fuse) {
+        gk.upd = *fuse;
+        return run.check(launch_gemm(dt, GemmKind::KV_UPDATE, gk, s), "persistent kv projection + small step");
+    }
     return run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection");
 }
 
@@ -315,8 +322,18 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
     RT_TRY(run.check(launch_update(dt, dh, u, s), "finalize position 1"));
 
     const size_t slab = (size_t)B * d->d_model * es;
+    // the blocked schedule's steps of 1, 2 and 4 pairs run inside the K/V projection (bf16, head_dim 64)
+    const bool fuse_small = mode == Mode::Blocked && dt == RT_BF16 && dh == 64;
     for (int32_t t = 1; t <= N; ++t) {
         const size_t at = (size_t)(t - 1) * slab;
+        const int32_t bt = block_of(t);
+        if (fuse_small && t < N && bt <= 4) {
+            u.kv0 = t - bt; u.nkv = bt; u.q0 = t; u.nq = (bt < N - t) ? bt : N - t;
+            u.init = (bt == t); u.fin = 1;
+            RT_TRY(enqueue_tail(d, w, p, base, L, B, a, (const char*)x + at, (char*)z + at, (char*)kc + at,
+                                (char*)vc + at, run, &u));
+            continue;
+        }
         RT_TRY(enqueue_tail(d, w, p, base, L, B, a, (const char*)x + at, (char*)z + at, (char*)kc + at,
                             (char*)vc + at, run));
         if (t == N) break;

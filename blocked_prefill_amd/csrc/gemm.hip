@@ -59,6 +59,96 @@ __device__ __forceinline__ void lds_barrier() {
 // chunk column fall in 16 different 4-bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// A small blocked step (blocks of 1, 2 or 4 pairs) run by the workgroup that
+// has just produced the newest key/value row of the block for `rows` batch
+// rows of one head (kvs: row r holds k then v, 64 each, as stored). The same
+// arithmetic, merge order and branch-free loads as the standalone small-step
+// kernel of update.hip: block keys oldest first (the newest from kvs), then
+// the position's ephemeral pair, then the stored state; one 8-lane group per
+// (batch row, query row) item.
+__device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16* kvs, int kvs_pitch, int64_t m0,
+                                                 int rows, int64_t B, int head, int tid, int nthreads) {
+    constexpr int DH = 64, G = 8;
+    const int64_t H = a.P / B;
+    const int64_t slab = a.P * DH;
+    const int lane = tid & (G - 1);
+    const int items = rows * a.nq;
+    for (int it = tid / G; it < items; it += nthreads / G) {
+        const int r = it % rows, i = it / rows;
+        const int64_t p = (m0 + r) * H + head;
+        const int64_t j = a.q0 + i;
+        const int64_t sidx = j * a.P + p;
+        const int64_t off = p * DH + lane * 8;
+        const bool merge_state = !a.init;
+        const bool finish = a.fin && i == 0;
+        const bf16* qp = (const bf16*)a.q + j * slab + off;
+        Raw8<bf16> qr, ker, ver, kn, vn;
+        Raw8<float> osr;
+        qr.load(qp);
+        const float* sp = merge_state ? a.m + sidx : (const float*)qp;
+        const float* lp = merge_state ? a.l + sidx : (const float*)qp;
+        const float ms_ld = *sp, ls_ld = *lp;
+        osr.load(merge_state ? a.o + sidx * DH + lane * 8 : (const float*)a.q);
+        ker.load(finish ? (const bf16*)a.k_eph + j * slab + off : qp);
+        ver.load(finish ? (const bf16*)a.v_eph + j * slab + off : qp);
+        kn.load(kvs + r * kvs_pitch + lane * 8);
+        vn.load(kvs + r * kvs_pitch + DH + lane * 8);
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = qr[e] * a.sigma2;
+        float mb = -INFINITY, lb = 0.f, ob[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        auto merge = [&](float d, const Raw8<bf16>& val) {
+            const float mn = fmaxf(mb, d);
+            const float c = fast_exp2(mb - mn);
+            const float pe = fast_exp2(d - mn);
+            lb = lb * c + pe;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] = ob[e] * c + pe * val[e];
+            mb = mn;
+        };
+        auto score = [&](const Raw8<bf16>& key) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += qv[e] * key[e];
+            return group_sum<G>(d);
+        };
+        for (int u = 0; u + 1 < a.nkv; ++u) {  // the block's older pairs, from the caches
+            Raw8<bf16> ko, vo;
+            ko.load((const bf16*)a.k + (int64_t)(a.kv0 + u) * slab + off);
+            vo.load((const bf16*)a.v + (int64_t)(a.kv0 + u) * slab + off);
+            merge(score(ko), vo);
+        }
+        merge(score(kn), vn);  // the newest pair, as just stored
+        {
+            const float d = score(ker);
+            merge(finish ? d : -INFINITY, ver);
+        }
+        {
+            const float msv = merge_state ? ms_ld : -INFINITY;
+            const float lsv = merge_state ? ls_ld : 0.f;
+            const float mn = fmaxf(msv, mb);
+            const float cs = fast_exp2(msv - mn), cb = fast_exp2(mb - mn);
+            lb = lsv * cs + lb * cb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] = (merge_state ? osr[e] : 0.f) * cs + ob[e] * cb;
+            mb = mn;
+        }
+        if (finish) {
+            const float inv = 1.0f / lb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ob[e] *= inv;
+            store8((bf16*)a.a_out + off, ob);
+            if (a.lse && lane == 0) a.lse[sidx] = mb + log2f(lb);
+        } else {
+            if (lane == 0) {
+                a.m[sidx] = mb;
+                a.l[sidx] = lb;
+            }
+            store8(a.o + sidx * DH + lane * 8, ob);
+        }
+    }
+}
+
 // C = epilogue(A * W^T) with A, W bf16 and K % 64 == 0, N % BN == 0.
 // K tiles of 64 are fetched into registers D tiles ahead of use (a ring of
 // D register stages, so D-1 tiles are in flight while one is multiplied),
@@ -93,6 +183,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     __shared__ __attribute__((aligned(16))) char smem_all[KS * 2 * STAGE];
     __shared__ float rs[BM];     // row scale (1/rms)
     __shared__ float qsum[(FLAGS & EPI_RMS_PARTS) ? BM * 16 : 1];  // per-quad sums of the RMS partials
+    // EPI_UPDATE: the tile's k|v rows as stored (bf16), read by the fused step
+    __shared__ __attribute__((aligned(16))) bf16 kvs[(FLAGS & EPI_UPDATE) ? BM * (BN + 8) : 8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int grp = tid / NTG, gtid = tid % NTG, wave = gtid >> 6;
@@ -101,7 +193,11 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     const int gq = lane >> 5;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int n0 = blockIdx.x * BN;
-    const int seg = n0 / g.seg_n;
+    // PAIRED: tile n holds rows n*BN/2 .. of W[0] (its left half) and of W[1] (its right half)
+    constexpr bool PAIRED = (FLAGS & EPI_PAIRKV) != 0;
+    constexpr int HB = BN / 2;
+    const int seg = PAIRED ? 0 : n0 / g.seg_n;
+    const int pcol = (n0 / BN) * HB;  // PAIRED: first column of this tile in each segment
     const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * g.K;
     const bf16* A = (const bf16*)g.A;
 
@@ -120,7 +216,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int s = NTG * i + gtid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-        w_src[i] = W + (int64_t)r * g.K + c * 8;
+        w_src[i] = PAIRED ? (const bf16*)g.W[r >= HB] + (int64_t)(pcol + r % HB) * g.K + c * 8
+                          : W + (int64_t)r * g.K + c * 8;
     }
 
     bf16x8 ra[D][LA], rw[D][LW];
@@ -324,6 +421,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
         const int64_t row = m0 + r;
         const bool ok = in_tile && row < g.M;
         const int col = n0 + c0;
+        // column within the output segment
+        const int ocol = PAIRED ? pcol + c0 % HB : col % g.seg_n;
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kg = 0; kg < KS; ++kg) {
@@ -345,15 +444,15 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
         if constexpr ((FLAGS & EPI_QKNORM) != 0) {
             // per-head RMS (query/key norm): a head's head_dim/8 runs sit in as many
             // consecutive lanes (BN is a multiple of head_dim); seg is uniform per workgroup
-            if ((g.qkn_mask >> seg) & 1) {
+            if ((g.qkn_mask >> (PAIRED ? (c0 >= HB) : seg)) & 1) {
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
                 for (int o = 1; o < g.head_dim / 8; o <<= 1) ss += __shfl_xor(ss, o, 64);
                 const float sc = rsqrtf(ss / (float)g.head_dim + g.eps);
-                const float* gg = g.qkn_gain[seg];
+                const float* gg = g.qkn_gain[PAIRED ? (c0 >= HB) : seg];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] *= sc * (gg ? gg[col % g.seg_n + e] : 1.f);
+                for (int e = 0; e < 8; ++e) v[e] *= sc * (gg ? gg[ocol + e] : 1.f);
             }
         }
         if constexpr (PREF_R) {
@@ -368,7 +467,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
         }
         float stored[8];
         if (ok) {
-            TC* dst = C + row * g.ldc + (col % g.seg_n);
+            TC* dst = (PAIRED ? (TC*)g.C[c0 >= HB] : C) + row * g.ldc + ocol;
             if constexpr (sizeof(TC) == 2) {
                 bf16x8 o;
 #pragma unroll
@@ -377,6 +476,8 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
                     stored[e] = (float)o[e];
                 }
                 *reinterpret_cast<bf16x8*>(dst) = o;
+                if constexpr ((FLAGS & EPI_UPDATE) != 0)
+                    *reinterpret_cast<bf16x8*>(&kvs[r * (BN + 8) + c0]) = o;
             } else {
                 store8((float*)dst, v);
 #pragma unroll
@@ -386,7 +487,7 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
                 bf16x8 o;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = (bf16)v[e];
-                *reinterpret_cast<bf16x8*>((bf16*)g.C2 + row * g.ldc + (col % g.seg_n)) = o;
+                *reinterpret_cast<bf16x8*>((bf16*)g.C2 + row * g.ldc + ocol) = o;
             }
         }
         if (FLAGS & EPI_ROWSS) {
@@ -400,6 +501,11 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
             if (ok && (x % 4) == 0) g.rss_out[row * (g.N / kRowSSTile) + col / kRowSSTile] = sq;
         }
     }
+    }
+    if constexpr ((FLAGS & EPI_UPDATE) != 0) {
+        static_assert((FLAGS & EPI_PAIRKV) && BN == 128 && sizeof(TC) == 2, "the fused step reads one head's k|v");
+        __syncthreads();  // kvs complete
+        fused_small_step(g.upd, kvs, BN + 8, m0, (int)min((int64_t)BM, g.M - m0), g.M, n0 / BN, tid, NT);
     }
 }
 
@@ -486,6 +592,14 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
             }
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
             break;
+        case GemmKind::KV_UPDATE:
+            if constexpr (KS <= 2) {
+                if (g.qkn_mask)
+                    return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_PAIRKV | EPI_UPDATE | EPI_QKNORM, 32, 128, 1, 4, D,
+                                    16, KS>(g, s);
+                return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_PAIRKV | EPI_UPDATE, 32, 128, 1, 4, D, 16, KS>(g, s);
+            }
+            break;
         case GemmKind::KV:
             if constexpr (KS <= 2) {
                 if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16, KS>(g, s);
@@ -500,7 +614,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
 // divides into an even number of 64-wide tiles per group, else fewer.
 static int k_groups(GemmKind kind, const GemmArgs& g) {
     if (g.M >= 4096) return 1;
-    int ks = kind == GemmKind::W2 ? 4 : (kind == GemmKind::WO || kind == GemmKind::KV) ? 2 : 1;
+    int ks = kind == GemmKind::W2 ? 4
+             : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2 : 1;
     const int kt = g.K / 64;
     while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
     return ks;
@@ -542,6 +657,7 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
             case GemmKind::W1: e = run_f32<float, EPI_RMS | EPI_GELU>(g, s); break;
             case GemmKind::W2: e = run_f32<float, EPI_RESID>(g, s); break;
             case GemmKind::KV: e = run_f32<float, EPI_RMS>(g, s); break;
+            case GemmKind::KV_UPDATE: return hipErrorInvalidValue;  // bf16 layers only
         }
         if (e != hipSuccess || !g.qkn_mask) return e;
         return qk_norm_f32(g, s);

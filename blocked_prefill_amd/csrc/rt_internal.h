@@ -72,6 +72,9 @@ enum : int {
     EPI_ROWSS = 16,     // write this tile's partial sum of squares of each stored row (rss_out)
     EPI_COPY = 32,      // also store the result as bf16 into C2
     EPI_QKNORM = 64,    // RMS-normalise each head_dim-wide head of the segments in qkn_mask
+    EPI_PAIRKV = 128,   // tile n holds columns n*BN/2.. of segment 0 (left half) and of segment 1 (right)
+    EPI_UPDATE = 256,   // (with EPI_PAIRKV, bf16, head_dim 64) then run upd, a small blocked step whose
+                        // newest key/value row is this product's output (see gemm.hip)
 };
 struct GemmArgs {
     const void* A;      // [M][lda]
@@ -93,6 +96,7 @@ struct GemmArgs {
     int32_t qkn_mask;            // bit s: normalise segment s per head (query/key norm); 0: none
     int32_t head_dim;            // head width of that norm
     const float* qkn_gain[3];    // [seg_n] gains per segment (nullptr: ones)
+    UpdateArgs upd;              // EPI_UPDATE: the step (block of 1, 2 or 4 pairs ending at this row)
 };
 // Column-tile width of the GEMMs whose epilogue writes row partial sums
 // (the number of partial sums per row is N / this width).
@@ -104,6 +108,7 @@ enum class GemmKind {
     W1,       // A = h (f32), RMS + GELU, C = g (T)
     W2,       // A = g (T), C = z (T), R = h (f32)
     KV,       // A = z (T), RMS, C = k|v (T)
+    KV_UPDATE,// KV (bf16, head_dim 64), then the small blocked step g.upd fused into the same launch
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
 bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K);
