@@ -216,7 +216,7 @@ __device__ __forceinline__ void lds_fence_barrier() {
 //
 // A workgroup of WAVES waves takes one (batch*head pair p, tile of 32*WAVES
 // queries); each wave owns 32 queries. The block's keys and values stream
-// through LDS in tiles of 64 positions, shared by the waves:
+// through LDS in tiles of KT positions, shared by the waves:
 //   S^T[kv][q] = K Q^T       v_mfma_f32_32x32x16_bf16, A = K rows, B = Q^T
 //   O^T[dh][q] += V^T P^T    A = V^T (transposed into LDS), B = P^T
 // With K's rows fed in an order that swaps bits 2 and 3 of the row index,
@@ -224,18 +224,22 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // positions per 16-position slice, which is exactly the B-operand layout of
 // the second product: P never leaves registers, and the softmax statistics
 // and the O^T rescale are lane-local (the two lanes q and q+32 share a query).
-// Blocks are dispatched so that all query tiles of a pair land on the same
-// XCD back to back, keeping the pair's keys/values in that XCD's L2.
+// Workgroups are dispatched so that each XCD takes one contiguous range of
+// (pair, query tile) items: an XCD's concurrent workgroups read neighbouring
+// 128-byte pieces of the position-major slabs, and all query tiles of a pair
+// run on the same XCD back to back, keeping its keys/values in that L2.
+// KT: key/value positions per LDS tile (32 or 64). V^T sits in LDS with its
+// 8-key chunks XOR-swizzled by the dh row's 8-row group, so that the
+// transposing stores of a wave fall into different banks.
 //
 // RAGGED: the block length need not be a multiple of 32 (decode, naive
 // schedule); the missing key rows of the last chunk are masked.
 // CAUSAL: plain causal attention (the Transformer layer's). Keys are the
 // queries' own positions (kv0 = q0 = 0); query i takes key rows 0..i and is
 // written to row i of a_out; no state is read or written.
-template <int WAVES, bool RAGGED, bool CAUSAL>
+template <int WAVES, int KT, bool RAGGED, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, int nqt) {
     constexpr int DH = 64;
-    constexpr int KT = 64;          // key/value positions per LDS tile
     constexpr int KSTR = DH + 8;    // bf16 per K row in LDS (16-byte pad)
     constexpr int VSTR = KT + 8;    // bf16 per V^T row in LDS
     constexpr int NT = 64 * WAVES;
@@ -248,15 +252,11 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     int64_t pair;
     int qtile;
     {
+        // workgroup i runs on XCD i % 8; the grid (P * nqt items) divides by 8 when P does
         const int64_t i = blockIdx.x;
-        if ((a.P & 7) == 0) {
-            const int64_t k = i >> 3;
-            pair = (k / nqt) * 8 + (i & 7);
-            qtile = (int)(k % nqt);
-        } else {
-            pair = i / nqt;
-            qtile = (int)(i % nqt);
-        }
+        const int64_t item = (a.P & 7) == 0 ? (i & 7) * ((int64_t)gridDim.x >> 3) + (i >> 3) : i;
+        pair = item / nqt;
+        qtile = (int)(item % nqt);
     }
     const int64_t slab = a.P * DH;
     const int wave_q0 = qtile * 32 * WAVES + wave * 32;
@@ -297,24 +297,53 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
     constexpr int KCH = KT * 8 / NT;        // 16-byte K chunks per thread per tile
     constexpr int VCH = (KT / 2) * 8 / NT;  // V row-pair chunks per thread per tile
     static_assert(KCH >= 1 && VCH >= 1 && (KT * 8) % NT == 0 && ((KT / 2) * 8) % NT == 0, "tile staging");
+    static_assert(KT == 32 || KT == 64, "key tile");
+    // whole tiles (the plain instance: the host guarantees nkv % KT == 0) are
+    // read at per-thread 32-bit byte offsets from the tile's first row
+    const uint32_t row_bytes = (uint32_t)(slab * 2);
+    uint32_t koff[KCH], voff[VCH];
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+        const int c = tid + NT * i;
+        koff[i] = (uint32_t)(c >> 3) * row_bytes + (uint32_t)(c & 7) * 16;
+    }
+#pragma unroll
+    for (int i = 0; i < VCH; ++i) {
+        const int c = tid + NT * i;
+        voff[i] = (uint32_t)((c >> 3) * 2) * row_bytes + (uint32_t)(c & 7) * 16;
+    }
     bf16x8 kreg[KCH], vreg[VCH][2];
     auto fetch = [&](int kt0) {
-        // rows past the block (a ragged last tile) repeat its last row: real,
-        // finite data whose scores are masked (weight exactly 0). The loads are
-        // unconditional so that they stay in flight across the tile's work.
-        const int last = ((nkv - kt0) < KT ? (nkv - kt0) : KT) - 1;
+        if constexpr (RAGGED || CAUSAL) {
+            // rows past the block (a ragged last tile) repeat its last row: real,
+            // finite data whose scores are masked (weight exactly 0). The loads are
+            // unconditional so that they stay in flight across the tile's work.
+            const int last = ((nkv - kt0) < KT ? (nkv - kt0) : KT) - 1;
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + NT * i, r = min(c >> 3, last), ch = (c & 7) * 8;
-            kreg[i] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
-        }
+            for (int i = 0; i < KCH; ++i) {
+                const int c = tid + NT * i, r = min(c >> 3, last), ch = (c & 7) * 8;
+                kreg[i] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)(kt0 + r) * slab + ch);
+            }
 #pragma unroll
-        for (int i = 0; i < VCH; ++i) {
-            const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
-            vreg[i][0] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0, last)) * slab + ch);
-            vreg[i][1] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0 + 1, last)) * slab + ch);
+            for (int i = 0; i < VCH; ++i) {
+                const int c = tid + NT * i, r0 = (c >> 3) * 2, ch = (c & 7) * 8;
+                vreg[i][0] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0, last)) * slab + ch);
+                vreg[i][1] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)(kt0 + min(r0 + 1, last)) * slab + ch);
+            }
+        } else {
+            const char* kb = (const char*)(kbase + (int64_t)kt0 * slab);
+            const char* vb = (const char*)(vbase + (int64_t)kt0 * slab);
+#pragma unroll
+            for (int i = 0; i < KCH; ++i) kreg[i] = *reinterpret_cast<const bf16x8*>(kb + koff[i]);
+#pragma unroll
+            for (int i = 0; i < VCH; ++i) {
+                vreg[i][0] = *reinterpret_cast<const bf16x8*>(vb + voff[i]);
+                vreg[i][1] = *reinterpret_cast<const bf16x8*>(vb + voff[i] + row_bytes);
+            }
         }
     };
+    // V^T element (dh row d, key column kc): the 8-key chunk index is XORed with (d / 8) % (KT / 8)
+    auto vt_at = [](int d, int kc) { return d * VSTR + ((((kc >> 3) ^ ((d >> 3) & (KT / 8 - 1)))) << 3) + (kc & 7); };
     fetch(0);
     for (int kt0 = 0; kt0 < nkv; kt0 += KT) {
         const int rows = (nkv - kt0) < KT ? (nkv - kt0) : KT;  // 1..64 (64 except the last tile)
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
                     bf16x2 w;
                     w[0] = vreg[i][0][e];
                     w[1] = vreg[i][1][e];
-                    *reinterpret_cast<bf16x2*>(&Vt[(ch + e) * VSTR + r0]) = w;
+                    *reinterpret_cast<bf16x2*>(&Vt[vt_at(ch + e, r0)]) = w;
                 }
             }
         }
@@ -405,12 +434,14 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
             }
             ps += __shfl_xor(ps, 32, 64);
             l_run += ps;
-            const bf16* v_lo = &Vt[ql * VSTR + c32 + 8 * g];
-            const bf16* v_hi = &Vt[(32 + ql) * VSTR + c32 + 8 * g];
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_lo), p0, o0, 0, 0, 0);
-            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_lo + 16), p1, o0, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_hi), p0, o1, 0, 0, 0);
-            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(v_hi + 16), p1, o1, 0, 0, 0);
+            const bf16x8 vlo0 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(ql, c32 + 8 * g)]);
+            const bf16x8 vlo1 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(ql, c32 + 8 * g + 16)]);
+            const bf16x8 vhi0 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(32 + ql, c32 + 8 * g)]);
+            const bf16x8 vhi1 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(32 + ql, c32 + 8 * g + 16)]);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vlo0, p0, o0, 0, 0, 0);
+            o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vlo1, p1, o0, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhi0, p0, o1, 0, 0, 0);
+            o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhi1, p1, o1, 0, 0, 0);
         }
     }
     if (!qvalid) return;
@@ -505,13 +536,21 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
 template <int WAVES, bool CAUSAL = false>
 static hipError_t launch_mfma(const UpdateArgs& a, hipStream_t s) {
     const int nqt = (a.nq + 32 * WAVES - 1) / (32 * WAVES);
-    const int64_t blocks = a.P * nqt;
-    if (!CAUSAL && a.nkv % 32 != 0)
-        hipLaunchKernelGGL((update_mfma_kernel<WAVES, true, false>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s, a,
-                           nqt);
-    else
-        hipLaunchKernelGGL((update_mfma_kernel<WAVES, false, CAUSAL>), dim3((uint32_t)blocks), dim3(64 * WAVES), 0, s,
-                           a, nqt);
+    const dim3 grid((uint32_t)(a.P * nqt)), block(64 * WAVES);
+    // the plain instances address a tile's rows with 32-bit byte offsets
+    const bool offsets_fit = (uint64_t)a.P * 64 * 2 * 64 <= 0xffffffffull;
+    if constexpr (CAUSAL) {
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, 64, false, true>), grid, block, 0, s, a, nqt);
+    } else if (!offsets_fit) {
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, 64, true, false>), grid, block, 0, s, a, nqt);
+    } else if (a.nkv % 64 == 0) {
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, 64, false, false>), grid, block, 0, s, a, nqt);
+    } else if (WAVES <= 2 && a.nkv % 32 == 0) {
+        // 32-row tiles (staged by at most 128 threads)
+        if constexpr (WAVES <= 2) hipLaunchKernelGGL((update_mfma_kernel<WAVES, 32, false, false>), grid, block, 0, s, a, nqt);
+    } else {
+        hipLaunchKernelGGL((update_mfma_kernel<WAVES, 64, true, false>), grid, block, 0, s, a, nqt);
+    }
     return hipGetLastError();
 }
 
