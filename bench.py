@@ -117,8 +117,9 @@ def traffic_summary(fetch_dir, write_dir):
         "#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/fetch -o run -- python3 bench.py --counters",
         "#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/write -o run -- python3 bench.py --counters",
         "#   python3 bench.py --traffic-summary gpurun_out/fetch gpurun_out/write",
-        "# bench.py --counters runs one layer forward, then that layer's 2047 update launches",
-        "# (the ones counted here), then a plain 1 GiB device copy (the calibration kernel).",
+        "# bench.py --counters fills q, k', v' and the persistent caches with random values, runs",
+        "# the layer's 2047 update launches t = 1..2047 (the ones counted here), then a plain",
+        "# 1 GiB device copy (the calibration kernel).",
         "#",
         f"# Calibration on the 1 GiB copy ({copy_bytes} bytes read, {copy_bytes} written):",
         f"#   FETCH_SIZE = {fk:.0f} KiB  -> bytes read    = FETCH_SIZE * 1024 * {ff:.4f}",
