@@ -5,7 +5,8 @@ package. The GPU library (blocked_prefill_amd) never imports it, and this
 package imports nothing from the library.
 
 The arithmetic lives in rt_oracle.c (naive schedule, IEEE double); this module
-marshals numpy arrays into it. schedule.py holds the blocked schedule's integer
+marshals numpy arrays into it. layer_backward.py holds the layer's gradient
+(the chain rule in numpy fp64 over rt_oracle.c's forward values). schedule.py holds the blocked schedule's integer
 rules and blocked_reference.py the pages' blocked algorithm in fp64, which pins
 the naive oracle (both are written from the Recurrent Transformer reading note,
 lshu.cn/news/403416, summary section 4.2).
