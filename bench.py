@@ -286,6 +286,75 @@ def backward(args):
                       "frac": round(flops / (ms * 1e-3) / 1e12 / 2500.0, 4)}))
 
 
+def layer_backward_bench(args):
+    """The RT layer's backward (rt_layer_backward) at the stack workload's layer
+    shape (B=512, N=2048, d=1024, 16x64 heads, F=4096, bf16): one layer forward
+    (its stored output z), then the backward timed (mean of 2 after 1 warm-up),
+    with z_bar ~ N(0,1). Algorithmic work: the batched recompute (projections
+    of x and z, W_o, W_1, the attention with its log-sum-exp), the per-position
+    adjoint products (W_kv^T, W_2^T, W_1^T, W_o^T), the attention backward, the
+    batched input adjoint and the weight gradients."""
+    import torch
+
+    import blocked_prefill_amd as rt
+    import rt_inputs
+    rt.load()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    wl = rt_inputs.WORKLOADS["stack6_d1024_b512_n2048"]
+    N, B, D, H, dh, F = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff
+    x = torch.from_numpy(rt_inputs.layer_input(wl)).to(torch.bfloat16).to(dev)
+    w = rt_inputs.layer_weights(wl, 0)
+    w = {n: torch.from_numpy(w[n]).to(torch.bfloat16).to(dev) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    attn = rt.AttnDesc(batch=B, seq_len=N, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=1.0 / math.sqrt(dh))
+    desc = rt.LayerDesc(attn=attn, d_model=D, d_ff=F, rms_eps=1e-6, residual_scale=1.0, flags=0)
+    z, kc, vc = (torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    ws_f = torch.empty(rt.rt_layer_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+    rt.rt_layer_forward(desc, w, x, z, kc, vc, ws_f, stream=stream)
+    torch.cuda.synchronize()
+    del ws_f, kc, vc
+    f32 = dict(dtype=torch.float32, device=dev)
+    z_bar = torch.randn((N, B, D), generator=torch.Generator(device=dev).manual_seed(9), **f32)
+    x_bar = torch.empty((N, B, D), **f32)
+    grads = {n: torch.empty(w[n].shape, **f32) for n in w}
+    grads["g_attn"] = torch.empty(D, **f32)
+    grads["g_mlp"] = torch.empty(D, **f32)
+    nbytes = rt.rt_layer_backward_workspace_bytes(desc)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    log(f"layer backward: workspace {nbytes / 2**30:.1f} GiB")
+    call = lambda: rt.rt_layer_backward(desc, w, x, z, z_bar, x_bar, grads, ws, stream=stream)
+    t0 = time.time()
+    call()
+    torch.cuda.synchronize()
+    log(f"layer backward warm-up {time.time() - t0:.2f}s")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 2
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    assert bool(torch.isfinite(x_bar).all()) and all(bool(torch.isfinite(g).all()) for g in grads.values())
+    NB, P = N * B, B * H
+    pairs = N * (N - 1) / 2
+    flops = {
+        "recompute_products": 2.0 * NB * D * (3 * D + 2 * D + D + F),
+        "recompute_attention": 4.0 * dh * P * (pairs + N),
+        "position_adjoint_products": 2.0 * NB * (2 * D * D + D * F + F * D + D * D),
+        "attention_backward": 10.0 * dh * P * pairs + 12.0 * dh * P * N,
+        "input_adjoint_product": 2.0 * NB * 3 * D * D,
+        "weight_gradients": 2.0 * NB * (6 * D * D + 2 * D * F),
+    }
+    total = sum(flops.values())
+    print(json.dumps({"layer_backward": "RT layer backward, B=512, N=2048, d=1024, 16x64 heads, F=4096, bf16",
+                      "ms": round(ms, 3), "tokens_per_s": round(B * N / (ms * 1e-3), 1),
+                      "alg_TFLOP": {k: round(v / 1e12, 3) for k, v in flops.items()},
+                      "TFLOP_s": round(total / (ms * 1e-3) / 1e12, 2), "bound": "mfma", "peak_TFLOP_s": 2500.0,
+                      "frac": round(total / (ms * 1e-3) / 1e12 / 2500.0, 4),
+                      "workspace_GiB": round(nbytes / 2**30, 2)}))
+
+
 def decode(args):
     """One decode step (a new position per sequence against the persistent KV
     cache) of the B=512, d=1024 layer after a 2048-position prefill: mean of
@@ -354,6 +423,8 @@ def main():
                     help="summarise two rocprofv3 counter passes over --counters (no GPU needed)")
     ap.add_argument("--backward", action="store_true",
                     help="attention backward of the blocked schedule at B=512, 16x64 heads, N=2048")
+    ap.add_argument("--layer-backward", action="store_true",
+                    help="the RT layer's backward at B=512, N=2048, d=1024 (one layer)")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
     args = ap.parse_args()
@@ -382,6 +453,8 @@ def main():
         return decode(args)
     if args.backward:
         return backward(args)
+    if args.layer_backward:
+        return layer_backward_bench(args)
     wl = rt_inputs.WORKLOADS[args.workload]
     N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
     scale = 1.0 / math.sqrt(dh)

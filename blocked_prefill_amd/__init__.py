@@ -15,7 +15,7 @@ __all__ = [
     "rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes",
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
     "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
-    "rt_last_error", "EXPORTED",
+    "rt_layer_backward_workspace_bytes", "rt_layer_backward", "LayerGrads", "rt_last_error", "EXPORTED",
     "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
 ]
 
@@ -33,7 +33,7 @@ library_path = os.path.join(_HERE, "librt_prefill.so")
 EXPORTED = ["rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes", "rt_layer_forward",
             "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
             "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
-            "rt_last_error"]
+            "rt_layer_backward_workspace_bytes", "rt_layer_backward", "rt_last_error"]
 
 
 class RtError(RuntimeError):
@@ -55,6 +55,10 @@ class LayerDesc(ctypes.Structure):
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp", "g_q",
                                                "g_k")]
+
+
+class LayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")]
 
 
 _lib = None
@@ -83,6 +87,8 @@ def load():
             "rt_layer_decode_step": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _i32, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, _vp],
             "rt_schedule_step": [_i32, _i32] + [ctypes.POINTER(_i32)] * 4,
+            "rt_layer_backward": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _vp, _vp, _vp, _vp,
+                                  ctypes.POINTER(LayerGrads), _vp, ctypes.c_size_t, _vp],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -92,6 +98,8 @@ def load():
         L.rt_layer_workspace_bytes.restype = ctypes.c_size_t
         L.rt_layer_decode_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.rt_layer_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.rt_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
+        L.rt_layer_backward_workspace_bytes.restype = ctypes.c_size_t
         L.rt_layer_plan_destroy.argtypes = [_vp]
         L.rt_layer_plan_destroy.restype = None
         L.rt_last_error.argtypes = []
@@ -188,6 +196,21 @@ def rt_layer_decode_step(desc: LayerDesc, weights, n_past: int, x_t, z_t, k_cach
     W = _weights(weights)
     _check(load().rt_layer_decode_step(ctypes.byref(desc), ctypes.byref(W), n_past, _ptr(x_t), _ptr(z_t),
                                        _ptr(k_cache), _ptr(v_cache), _ptr(workspace), ws, _stream(stream)))
+
+
+def rt_layer_backward_workspace_bytes(desc: LayerDesc) -> int:
+    return int(load().rt_layer_backward_workspace_bytes(ctypes.byref(desc)))
+
+
+def rt_layer_backward(desc: LayerDesc, weights, x, z, z_bar, x_bar, grads, workspace, workspace_bytes=None,
+                      stream=None):
+    """grads: a LayerGrads or a dict of fp32 tensors by name (w_q .. w_2 required; g_attn, g_mlp optional)."""
+    ws = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    W = _weights(weights)
+    G = grads if isinstance(grads, LayerGrads) else LayerGrads(
+        **{n: _ptr(grads.get(n)) for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")})
+    _check(load().rt_layer_backward(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(z), _ptr(z_bar), _ptr(x_bar),
+                                    ctypes.byref(G), _ptr(workspace), ws, _stream(stream)))
 
 
 class Plan:

@@ -52,7 +52,9 @@ def build(verbose: bool = False) -> str:
         with ThreadPoolExecutor(workers) as ex:
             for f in [ex.submit(_run, cmd, verbose) for _, _, cmd in jobs]:
                 f.result()
-        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *[o for _, o, _ in jobs], "-o", LIB + ".tmp"], verbose)
+        # rocBLAS: the backward's weight gradients (plain GEMMs reducing over positions x rows)
+        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *[o for _, o, _ in jobs], "-lrocblas",
+              "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 

@@ -379,6 +379,242 @@ rt_status enqueue_decode(const rt_layer_desc* d, const rt_layer_weights* w, int3
                         transformer ? nullptr : vt, run);
 }
 
+// ---------------------------------------------------------------- backward
+
+rt_status check_backward(const rt_layer_desc* d) {
+    RT_TRY(check_layer(d));
+    if (d->flags & RT_FLAG_TRANSFORMER) return fail(RT_ERR_UNSUPPORTED, "the backward covers the RT layer only");
+    if (d->flags & RT_FLAG_QK_NORM) return fail(RT_ERR_UNSUPPORTED, "the backward does not cover RT_FLAG_QK_NORM");
+    return RT_OK;
+}
+
+// Workspace of the layer backward (byte offsets, 256-aligned); NB = N*B rows.
+struct BLayout {
+    size_t wq, wk, wv, w1;                 // gain-folded weights (the recompute's products)
+    size_t wkvT, w2T, w1T, woT, wqkvT;     // transposed weights (the adjoint products)
+    size_t q, ke, ve, kc, vc, a;           // [NB][d] dtype: recomputed forward values
+    size_t m, l, lse, delta;               // [N][P] fp32
+    size_t o;                              // [NB][d] fp32: attention state, later the adjoint of RMS_attn(x)
+    size_t h;                              // [NB][d] fp32
+    size_t hb;                             // [NB][d] bf16 copy of h (bf16 layers)
+    size_t hss;                            // [NB][d/32] fp32 partial sums of h^2 (bf16 layers)
+    size_t u;                              // [NB][F] dtype: W_1 RMS(h), later GELU of it
+    size_t kbar, vbar, qbar, kebar, vebar, abar, uzbar, mbar;  // [NB][d] fp32 adjoints
+    size_t zbs, hbs;                       // [NB][d] dtype: rho * z_bar(total), rho * h_bar
+    size_t ubar;                           // [NB][F] dtype
+    size_t rz, rh, rx;                     // [NB] fp32: 1/rms of z, h, x
+    size_t pkv;                            // [B][2d] dtype: k_bar|v_bar of one position
+    size_t zt;                             // [B][d] fp32: z_bar(total) of one position
+    size_t gb;                             // [B][F] fp32: W_2^T adjoint of one position
+    size_t qkvb, kvb;                      // [NB][3d], [NB][2d] dtype: adjoints as product operands
+    size_t gpart;                          // gain-gradient partial sums
+    size_t total;
+};
+
+BLayout blayout_of(const rt_layer_desc* d) {
+    const size_t es = elem_bytes(d->attn.dtype);
+    const size_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, D = d->d_model, F = d->d_ff;
+    const size_t NB = N * B, P = B * H;
+    BLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return at;
+    };
+    L.wq = take(D * D * es); L.wk = take(D * D * es); L.wv = take(D * D * es); L.w1 = take(F * D * es);
+    L.wkvT = take(D * 2 * D * es); L.w2T = take(F * D * es); L.w1T = take(D * F * es); L.woT = take(D * D * es);
+    L.wqkvT = take(D * 3 * D * es);
+    L.q = take(NB * D * es); L.ke = take(NB * D * es); L.ve = take(NB * D * es);
+    L.kc = take(NB * D * es); L.vc = take(NB * D * es); L.a = take(NB * D * es);
+    L.m = take(N * P * 4); L.l = take(N * P * 4); L.lse = take(N * P * 4); L.delta = take(N * P * 4);
+    L.o = take(NB * D * 4);
+    L.h = take(NB * D * 4);
+    L.hb = take(NB * D * 2);
+    L.hss = take(D / rt::kRowSSTile * NB * 4 + 4);
+    L.u = take(NB * F * es);
+    L.kbar = take(NB * D * 4); L.vbar = take(NB * D * 4); L.qbar = take(NB * D * 4);
+    L.kebar = take(NB * D * 4); L.vebar = take(NB * D * 4); L.abar = take(NB * D * 4);
+    L.uzbar = take(NB * D * 4); L.mbar = take(NB * D * 4);
+    L.zbs = take(NB * D * es); L.hbs = take(NB * D * es);
+    L.ubar = take(NB * F * es);
+    L.rz = take(NB * 4); L.rh = take(NB * 4); L.rx = take(NB * 4);
+    L.pkv = take(B * 2 * D * es);
+    L.zt = take(B * D * 4);
+    L.gb = take(B * F * 4);
+    L.qkvb = take(NB * 3 * D * es);
+    L.kvb = take(NB * 2 * D * es);
+    L.gpart = take((size_t)rt::gain_grad_blocks((int64_t)NB) * D * 4);
+    L.total = off;
+    return L;
+}
+
+rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights* w, const void* x, const void* z,
+                                 const float* z_bar, float* x_bar, const rt_layer_grads* gr, void* ws,
+                                 hipStream_t s, bool debug) {
+    using namespace rt;
+    Launcher run{s, debug};
+    const rt_dtype dt = d->attn.dtype;
+    const bool b16 = dt == RT_BF16;
+    const size_t es = elem_bytes(dt);
+    const int32_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, dh = d->attn.head_dim;
+    const int32_t D = d->d_model, F = d->d_ff;
+    const int64_t NB = (int64_t)N * B, P = (int64_t)B * H;
+    const float rho = d->residual_scale, eps = d->rms_eps;
+    const BLayout L = blayout_of(d);
+    char* base = (char*)ws;
+    auto at = [&](size_t off) { return (void*)(base + off); };
+    auto f32 = [&](size_t off) { return (float*)(base + off); };
+
+    // ---- weights: gain-folded for the recompute, transposed for the adjoint products
+    Layout fl{};
+    fl.wq = L.wq; fl.wk = L.wk; fl.wv = L.wv; fl.w1 = L.w1;
+    Projections p;
+    RT_TRY(enqueue_fold(d, w, base, fl, run, &p));
+    RT_TRY(run.check(launch_transpose(dt, w->w_k, D, D, at(L.wkvT), 2 * D, 0, s), "transpose W_k"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_v, D, D, at(L.wkvT), 2 * D, D, s), "transpose W_v"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_2, D, F, at(L.w2T), D, 0, s), "transpose W_2"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_1, F, D, at(L.w1T), F, 0, s), "transpose W_1"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_o, D, D, at(L.woT), D, 0, s), "transpose W_o"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_q, D, D, at(L.wqkvT), 3 * D, 0, s), "transpose W_q"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_k, D, D, at(L.wqkvT), 3 * D, D, s), "transpose W_k"));
+    RT_TRY(run.check(launch_transpose(dt, w->w_v, D, D, at(L.wqkvT), 3 * D, 2 * D, s), "transpose W_v"));
+
+    // ---- recompute, batched over all N*B rows
+    RT_TRY(enqueue_qkv(d, w, p, x, NB, at(L.q), at(L.ke), at(L.ve), run));
+    {   // the persistent pairs from the stored outputs
+        GemmArgs gk{};
+        gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = at(L.kc); gk.C[1] = at(L.vc);
+        gk.ldc = D; gk.seg_n = D; gk.eps = eps; gk.M = NB; gk.N = 2 * D; gk.K = D;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::QKV, gk, s), "persistent pairs from z"));
+    }
+    {   // the blocked attention with each query's log-sum-exp (finishing query t+1 in step t)
+        UpdateArgs u{};
+        u.q = at(L.q); u.k = at(L.kc); u.v = at(L.vc); u.k_eph = at(L.ke); u.v_eph = at(L.ve);
+        u.m = f32(L.m); u.l = f32(L.l); u.o = f32(L.o); u.lse = f32(L.lse); u.P = P;
+        u.sigma2 = d->attn.softmax_scale * kLog2eHost;
+        const size_t slab = (size_t)B * D * es;
+        u.a_out = at(L.a); u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
+        RT_TRY(run.check(launch_update(dt, dh, u, s), "attention recompute"));
+        for (int32_t t = 1; t < N; ++t) {
+            const int32_t b = block_of(t);
+            u.a_out = base + L.a + (size_t)t * slab;
+            u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
+            u.init = (b == t); u.fin = 1;
+            RT_TRY(run.check(launch_update(dt, dh, u, s), "attention recompute"));
+        }
+    }
+    {   // h = x + rho W_o a (and, in bf16 layers, its bf16 copy and partial sums of h^2)
+        GemmArgs go{};
+        go.A = at(L.a); go.lda = D; go.W[0] = w->w_o; go.C[0] = f32(L.h); go.ldc = D; go.seg_n = D;
+        go.R = x; go.ldr = D; go.rscale = rho; go.M = NB; go.N = D; go.K = D;
+        if (b16) { go.C2 = at(L.hb); go.rss_out = f32(L.hss); }
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "h recompute"));
+        GemmArgs g1{};  // u = W_1 RMS_mlp(h), before the GELU
+        g1.A = b16 ? at(L.hb) : (const void*)f32(L.h); g1.lda = D; g1.W[0] = p.w1; g1.C[0] = at(L.u);
+        g1.ldc = F; g1.seg_n = F; g1.eps = eps; g1.M = NB; g1.N = F; g1.K = D;
+        if (b16) { g1.rss_in = f32(L.hss); g1.n_parts = D / kRowSSTile; }
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::W1_PRE, g1, s), "u recompute"));
+    }
+
+    // ---- positions in reverse
+    RT_TRY(run.check(launch_zero_f32(f32(L.kbar), NB * D, s), "clear k_bar"));
+    RT_TRY(run.check(launch_zero_f32(f32(L.vbar), NB * D, s), "clear v_bar"));
+    BackwardArgs bw{};
+    bw.q = at(L.q); bw.k_eph = at(L.ke); bw.v_eph = at(L.ve); bw.k = at(L.kc); bw.v = at(L.vc); bw.a = at(L.a);
+    bw.lse = f32(L.lse); bw.a_bar = f32(L.abar); bw.q_bar = f32(L.qbar); bw.k_eph_bar = f32(L.kebar);
+    bw.v_eph_bar = f32(L.vebar); bw.k_bar = f32(L.kbar); bw.v_bar = f32(L.vbar); bw.delta = f32(L.delta);
+    bw.P = P; bw.n_pos = N; bw.sigma = d->attn.softmax_scale; bw.sigma2 = d->attn.softmax_scale * kLog2eHost;
+    bw.kv_accumulate = 1;
+    auto plain = [&](const void* A, int64_t lda, const void* W, int n, int k, float* C, const char* what) {
+        GemmArgs g{};
+        g.A = A; g.lda = lda; g.W[0] = W; g.C[0] = C; g.ldc = n; g.seg_n = n; g.M = B; g.N = n; g.K = k;
+        return run.check(launch_gemm(dt, GemmKind::PLAIN, g, s), what);
+    };
+    const size_t rowsD = (size_t)B * D, rowsF = (size_t)B * F;
+    for (int32_t j = N - 1; j >= 0; --j) {
+        if (j + 1 < N) {  // step t = j + 1: keys (t-b, t] against queries (t, t+b]
+            const int32_t t = j + 1, b = block_of(t);
+            RT_TRY(run.check(launch_backward_step(dt, dh, bw, t - b, b, t, (b < N - t) ? b : N - t, s),
+                             "attention rectangle"));
+        }
+        float* kb = f32(L.kbar) + j * rowsD;
+        float* vb = f32(L.vbar) + j * rowsD;
+        float* uzb = f32(L.uzbar) + j * rowsD;
+        RT_TRY(run.check(launch_pack(dt, at(L.pkv), 2 * D, kb, vb, nullptr, 2, B, D, 1.f, s), "pack k_bar|v_bar"));
+        RT_TRY(plain(at(L.pkv), 2 * D, at(L.wkvT), D, 2 * D, uzb, "W_kv^T product"));
+        void* zbs = base + L.zbs + j * rowsD * es;
+        RT_TRY(run.check(launch_rms_bwd(dt, dt, (const char*)z + j * rowsD * es, uzb, w->g_attn, eps,
+                                        z_bar + j * rowsD, f32(L.zt), zbs, rho, f32(L.rz) + (int64_t)j * B, B, D, s),
+                         "RMS_attn adjoint of z"));
+        RT_TRY(plain(zbs, D, at(L.w2T), F, D, f32(L.gb), "W_2^T product"));
+        void* ub = base + L.ubar + j * rowsF * es;
+        RT_TRY(run.check(launch_gelu_bwd(dt, f32(L.gb), base + L.u + j * rowsF * es, ub, (int64_t)rowsF, s),
+                         "GELU adjoint"));
+        float* mb = f32(L.mbar) + j * rowsD;
+        RT_TRY(plain(ub, F, at(L.w1T), D, F, mb, "W_1^T product"));
+        void* hbs = base + L.hbs + j * rowsD * es;
+        RT_TRY(run.check(launch_rms_bwd(RT_F32, dt, f32(L.h) + j * rowsD, mb, w->g_mlp, eps, f32(L.zt),
+                                        x_bar + j * rowsD, hbs, rho, f32(L.rh) + (int64_t)j * B, B, D, s),
+                         "RMS_mlp adjoint of h"));
+        RT_TRY(plain(hbs, D, at(L.woT), D, D, f32(L.abar) + j * rowsD, "W_o^T product"));
+        {   // query j's own pass: D_j, the ephemeral pair's gradients, q_bar's first term
+            BackwardArgs bj = bw;
+            const size_t eo = (size_t)j * rowsD * es;
+            bj.q = base + L.q + eo; bj.k_eph = base + L.ke + eo; bj.v_eph = base + L.ve + eo; bj.a = base + L.a + eo;
+            bj.lse = f32(L.lse) + (int64_t)j * P; bj.delta = f32(L.delta) + (int64_t)j * P;
+            bj.a_bar = f32(L.abar) + j * rowsD; bj.q_bar = f32(L.qbar) + j * rowsD;
+            bj.k_eph_bar = f32(L.kebar) + j * rowsD; bj.v_eph_bar = f32(L.vebar) + j * rowsD;
+            bj.n_pos = 1;
+            RT_TRY(run.check(launch_backward_prep(dt, dh, bj, s), "query pass"));
+        }
+    }
+
+    // ---- batched: the input's adjoint through RMS_attn(x)
+    float* uxb = f32(L.o);  // (the attention state is no longer needed)
+    RT_TRY(run.check(launch_pack(dt, at(L.qkvb), 3 * D, f32(L.qbar), f32(L.kebar), f32(L.vebar), 3, NB, D, 1.f, s),
+                     "pack q_bar|k'_bar|v'_bar"));
+    {
+        GemmArgs g{};
+        g.A = at(L.qkvb); g.lda = 3 * D; g.W[0] = at(L.wqkvT); g.C[0] = uxb; g.ldc = D; g.seg_n = D;
+        g.M = NB; g.N = D; g.K = 3 * D;
+        RT_TRY(run.check(launch_gemm(dt, GemmKind::PLAIN, g, s), "W_qkv^T product"));
+    }
+    RT_TRY(run.check(launch_rms_bwd(dt, dt, x, uxb, w->g_attn, eps, x_bar, x_bar, nullptr, 1.f, f32(L.rx), NB, D, s),
+                     "RMS_attn adjoint of x"));
+
+    // ---- weight gradients: the products' inputs, materialised (q, k', v' are no longer needed)
+    void* ux = at(L.q);
+    void* uz = at(L.ke);
+    void* mm = at(L.ve);
+    RT_TRY(run.check(launch_rms_apply(dt, dt, x, w->g_attn, eps, ux, NB, D, s), "RMS_attn(x)"));
+    RT_TRY(run.check(launch_rms_apply(dt, dt, z, w->g_attn, eps, uz, NB, D, s), "RMS_attn(z)"));
+    RT_TRY(run.check(launch_rms_apply(RT_F32, dt, f32(L.h), w->g_mlp, eps, mm, NB, D, s), "RMS_mlp(h)"));
+    RT_TRY(run.check(launch_pack(dt, at(L.kvb), 2 * D, f32(L.kbar), f32(L.vbar), nullptr, 2, NB, D, 1.f, s),
+                     "pack k_bar|v_bar"));
+    RT_TRY(run.check(launch_gelu_inplace(dt, at(L.u), NB * F, s), "GELU(u)"));
+    const char* qkvb = base + L.qkvb;
+    const char* kvb = base + L.kvb;
+    RT_TRY(run.check(weight_grad(dt, qkvb, 3 * D, ux, D, NB, D, D, gr->w_q, false, s), "W_q gradient"));
+    RT_TRY(run.check(weight_grad(dt, qkvb + D * es, 3 * D, ux, D, NB, D, D, gr->w_k, false, s), "W_k gradient"));
+    RT_TRY(run.check(weight_grad(dt, kvb, 2 * D, uz, D, NB, D, D, gr->w_k, true, s), "W_k gradient"));
+    RT_TRY(run.check(weight_grad(dt, qkvb + 2 * D * es, 3 * D, ux, D, NB, D, D, gr->w_v, false, s), "W_v gradient"));
+    RT_TRY(run.check(weight_grad(dt, kvb + D * es, 2 * D, uz, D, NB, D, D, gr->w_v, true, s), "W_v gradient"));
+    RT_TRY(run.check(weight_grad(dt, at(L.hbs), D, at(L.a), D, NB, D, D, gr->w_o, false, s), "W_o gradient"));
+    RT_TRY(run.check(weight_grad(dt, at(L.ubar), F, mm, D, NB, F, D, gr->w_1, false, s), "W_1 gradient"));
+    RT_TRY(run.check(weight_grad(dt, at(L.zbs), D, at(L.u), F, NB, D, F, gr->w_2, false, s), "W_2 gradient"));
+    if (gr->g_attn) {
+        RT_TRY(run.check(launch_gain_grad(dt, uxb, x, f32(L.rx), NB, D, f32(L.gpart), gr->g_attn, 0, s), "g_attn"));
+        RT_TRY(run.check(launch_gain_grad(dt, f32(L.uzbar), z, f32(L.rz), NB, D, f32(L.gpart), gr->g_attn, 1, s),
+                         "g_attn"));
+    }
+    if (gr->g_mlp)
+        RT_TRY(run.check(launch_gain_grad(RT_F32, f32(L.mbar), f32(L.h), f32(L.rh), NB, D, f32(L.gpart), gr->g_mlp,
+                                          0, s),
+                         "g_mlp"));
+    return RT_OK;
+}
+
 }  // namespace
 
 struct rt_plan {
@@ -546,6 +782,43 @@ rt_status rt_attn_backward(const rt_attn_desc* desc, const void* q, const void* 
 size_t rt_layer_workspace_bytes(const rt_layer_desc* desc) {
     if (check_layer(desc) != RT_OK) return 0;
     return layout_of(desc, mode_of(desc)).total;
+}
+
+size_t rt_layer_backward_workspace_bytes(const rt_layer_desc* desc) {
+    if (check_backward(desc) != RT_OK) return 0;
+    return blayout_of(desc).total;
+}
+
+rt_status rt_layer_backward(const rt_layer_desc* desc, const rt_layer_weights* w, const void* x, const void* z,
+                            const float* z_bar, float* x_bar, const rt_layer_grads* grads, void* workspace,
+                            size_t workspace_bytes, rt_stream_t stream) {
+    RT_TRY(check_backward(desc));
+    if (!w) return fail(RT_ERR_INVALID_ARG, "weights is NULL");
+    {
+        const void* ps[] = {w->w_q, w->w_k, w->w_v, w->w_o, w->w_1, w->w_2, x, z, z_bar, x_bar, workspace};
+        const char* names[] = {"w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "x", "z", "z_bar", "x_bar", "workspace"};
+        for (int i = 0; i < 11; ++i) {
+            if (!ps[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", names[i]);
+            if (!aligned16(ps[i])) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+        }
+        if (((uintptr_t)workspace & 255u) != 0) return fail(RT_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+        if ((w->g_attn && !aligned16(w->g_attn)) || (w->g_mlp && !aligned16(w->g_mlp)))
+            return fail(RT_ERR_INVALID_ARG, "gains must be 16-byte aligned");
+    }
+    if (!grads) return fail(RT_ERR_INVALID_ARG, "grads is NULL");
+    const float* gp[] = {grads->w_q, grads->w_k, grads->w_v, grads->w_o, grads->w_1, grads->w_2};
+    const char* gn[] = {"grads->w_q", "grads->w_k", "grads->w_v", "grads->w_o", "grads->w_1", "grads->w_2"};
+    for (int i = 0; i < 6; ++i) {
+        if (!gp[i]) return fail(RT_ERR_INVALID_ARG, "%s is NULL", gn[i]);
+        if (!aligned16(gp[i])) return fail(RT_ERR_INVALID_ARG, "%s is not 16-byte aligned", gn[i]);
+    }
+    if ((grads->g_attn && ((uintptr_t)grads->g_attn & 3u)) || (grads->g_mlp && ((uintptr_t)grads->g_mlp & 3u)))
+        return fail(RT_ERR_INVALID_ARG, "gain gradients must be 4-byte aligned");
+    const size_t need = blayout_of(desc).total;
+    if (workspace_bytes < need)
+        return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    return enqueue_layer_backward(desc, w, x, z, z_bar, x_bar, grads, workspace, (hipStream_t)stream,
+                                  (desc->flags & RT_FLAG_DEBUG_SYNC) != 0);
 }
 
 size_t rt_layer_decode_workspace_bytes(const rt_layer_desc* desc) {

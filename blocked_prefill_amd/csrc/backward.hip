@@ -103,7 +103,7 @@ __device__ __forceinline__ void bwd_kv_item(const BackwardArgs& b, int64_t item,
     }
     float* kr = b.k_bar + i * slab + off;
     float* vr = b.v_bar + i * slab + off;
-    if (i != kv0 + nkv - 1) {
+    if (b.kv_accumulate || i != kv0 + nkv - 1) {
         float ko[8], vo[8];
         load8(kr, ko);
         load8(vr, vo);
@@ -422,7 +422,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
         }
     }
     if (!kvalid) return;
-    const bool first = krow_local == nkv - 1;  // the block's last row: this step's first visit
+    // the block's last row: this step's first visit when steps run in forward order
+    const bool first = !b.kv_accumulate && krow_local == nkv - 1;
     float* kr = b.k_bar + i_row * slab + pair * DH;
     float* vr = b.v_bar + i_row * slab + pair * DH;
 #pragma unroll

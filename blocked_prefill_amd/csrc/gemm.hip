@@ -606,6 +606,17 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
                 return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
             }
             break;
+        case GemmKind::W1_PRE:
+            if constexpr (KS == 1)
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(g, s)
+                           : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
+            break;
+        case GemmKind::PLAIN:
+            if constexpr (KS == 1) {
+                if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(g, s);
+            }
+            if (!big) return run_pipe<float, float, 0, 64, 64, 2, 2, D, 16, KS>(g, s);
+            break;
     }
     return hipErrorInvalidValue;
 }
@@ -615,7 +626,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
 static int k_groups(GemmKind kind, const GemmArgs& g) {
     if (g.M >= 4096) return 1;
     int ks = kind == GemmKind::W2 ? 4
-             : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2 : 1;
+             : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2
+             : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : 1;
     const int kt = g.K / 64;
     while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
     return ks;
@@ -658,6 +670,8 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
             case GemmKind::W2: e = run_f32<float, EPI_RESID>(g, s); break;
             case GemmKind::KV: e = run_f32<float, EPI_RMS>(g, s); break;
             case GemmKind::KV_UPDATE: return hipErrorInvalidValue;  // bf16 layers only
+            case GemmKind::W1_PRE: e = run_f32<float, EPI_RMS>(g, s); break;
+            case GemmKind::PLAIN: e = run_f32<float, 0>(g, s); break;
         }
         if (e != hipSuccess || !g.qkn_mask) return e;
         return qk_norm_f32(g, s);

@@ -51,12 +51,14 @@ struct BackwardArgs {
     int32_t n_pos;
     float sigma;                                // softmax_scale (natural units)
     float sigma2;                               // softmax_scale * log2(e)
+    int32_t kv_accumulate;                      // 0: a step sets its block's last k_bar/v_bar row (forward
+                                                // step order); 1: every row accumulates (rows pre-zeroed)
 };
 // Per-query pass over all positions: delta, the ephemeral pair's gradients, q_bar's ephemeral term.
 hipError_t launch_backward_prep(rt_dtype dt, int head_dim, const BackwardArgs& b, hipStream_t s);
 // Step t of the blocked schedule, reversed: the block of keys (kv0, kv0+nkv] against the queries
-// (q0, q0+nq]; k_bar/v_bar rows of the block accumulate (row kv0+nkv-1, first touched here, is set),
-// q_bar rows of the queries accumulate.
+// (q0, q0+nq]; k_bar/v_bar rows of the block accumulate (row kv0+nkv-1, first touched here when
+// steps run in forward order, is set unless kv_accumulate), q_bar rows of the queries accumulate.
 hipError_t launch_backward_step(rt_dtype dt, int head_dim, const BackwardArgs& b, int32_t kv0, int32_t nkv,
                                 int32_t q0, int32_t nq, hipStream_t s);
 // Zero rows [row0, row0 + rows) of k_bar and v_bar (pairs no query reads).
@@ -109,8 +111,39 @@ enum class GemmKind {
     W2,       // A = g (T), C = z (T), R = h (f32)
     KV,       // A = z (T), RMS, C = k|v (T)
     KV_UPDATE,// KV (bf16, head_dim 64), then the small blocked step g.upd fused into the same launch
+    W1_PRE,   // A = h (bf16 copy with RMS partials, or fp32), RMS, C = W_1 RMS(h) before the GELU (T)
+    PLAIN,    // C (fp32) = A (T) * W^T, no epilogue (the backward's adjoint products)
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
+
+// ---- the layer backward's pieces (layer_backward.hip)
+// dst[c][col0 + r] = src[r][c] for src [rows][cols] (dtype dt), dst row stride ldd.
+hipError_t launch_transpose(rt_dtype dt, const void* src, int64_t rows, int64_t cols, void* dst, int64_t ldd,
+                            int64_t col0, hipStream_t s);
+// dst[r][s*D + c] = scale * src_s[r][c] for s < nsrc (fp32 sources [rows][D], dst dtype dt, row stride ldd).
+hipError_t launch_pack(rt_dtype dt, void* dst, int64_t ldd, const float* s0, const float* s1, const float* s2,
+                       int nsrc, int64_t rows, int D, float scale, hipStream_t s);
+// Per row of x [rows][D]: out = base + the adjoint of x for y = g x / rms(x) given y_bar
+// (base, g may be null: 0, ones); out2 (nullable) = scale2 * out in out2_dt; rinv_out (nullable) = 1/rms.
+hipError_t launch_rms_bwd(rt_dtype x_dt, rt_dtype out2_dt, const void* x, const float* ybar, const float* g,
+                          float eps, const float* base, float* out, void* out2, float scale2, float* rinv_out,
+                          int64_t rows, int D, hipStream_t s);
+// out = g x / rms(x) per row, in out_dt.
+hipError_t launch_rms_apply(rt_dtype x_dt, rt_dtype out_dt, const void* x, const float* g, float eps, void* out,
+                            int64_t rows, int D, hipStream_t s);
+// out = gbar * GELU'(u) (u, out in dt), elementwise over n.
+hipError_t launch_gelu_bwd(rt_dtype dt, const float* gbar, const void* u, void* out, int64_t n, hipStream_t s);
+// u = GELU(u) in place.
+hipError_t launch_gelu_inplace(rt_dtype dt, void* u, int64_t n, hipStream_t s);
+// Gain gradient: out[c] (+)= sum_r y_bar[r][c] x[r][c] rinv[r]; part holds gain_grad_blocks(rows) * D floats.
+constexpr int kGainRowsPerBlock = 256;
+int64_t gain_grad_blocks(int64_t rows);
+hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, const float* rinv, int64_t rows, int D,
+                            float* part, float* out, int accumulate, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+// out[o][i] (+)= sum_r abar[r][o] u[r][i] (abar row stride lda, u row stride ldu, both in dt; out fp32 [O][I]).
+hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u, int64_t ldu, int64_t R, int O,
+                       int I, float* out, bool accumulate, hipStream_t s);
 bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K);
 
 // W_out[r][c] = W[r][c] * g[c] (fold an RMS gain into the following projection).

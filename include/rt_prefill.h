@@ -229,6 +229,58 @@ rt_status rt_layer_forward(const rt_layer_desc* desc, const rt_layer_weights* w,
                            void* workspace, size_t workspace_bytes, rt_stream_t stream);
 
 /*
+ * Gradients of a layer's parameters, fp32, each shaped as its parameter:
+ * w_q, w_k, w_v, w_o [d][d], w_1 [F][d], w_2 [d][F], g_attn, g_mlp [d].
+ * The six weight gradients are required; a gain gradient may be NULL (then
+ * it is not computed). Gains absent from rt_layer_weights are ones, and their
+ * gradients are still defined.
+ */
+typedef struct {
+    float *w_q, *w_k, *w_v, *w_o, *w_1, *w_2;
+    float *g_attn, *g_mlp;
+} rt_layer_grads;
+
+/*
+ * rt_layer_backward_workspace_bytes -- device workspace of rt_layer_backward,
+ * or 0 for an invalid or unsupported descriptor.
+ */
+size_t rt_layer_backward_workspace_bytes(const rt_layer_desc* desc);
+
+/*
+ * rt_layer_backward -- gradient of L = sum(z_bar * z) for the RT layer map of
+ * rt_layer_forward. The pages give the backward only as an idea: it can be
+ * batched outside the position loop, with the persistent pairs rebuilt from
+ * the stored outputs (translated paper section 6.1; section 6.4 is a heading
+ * without a body). The gradient here is the chain rule:
+ *   - recompute, batched over all N*B rows: q, k', v' from x; the persistent
+ *     k, v from the given z; the blocked attention with each query's
+ *     log-sum-exp; h; the MLP's pre-activation u;
+ *   - positions in reverse: step t's attention rectangle (its queries are all
+ *     differentiated by then, so row t's k_bar, v_bar are complete), then
+ *       z_bar_t += RMS_attn'(z_t)^T (W_k^T k_bar_t + W_v^T v_bar_t)
+ *       u_bar = rho (W_2^T z_bar_t) * GELU'(u_t)
+ *       h_bar = z_bar_t + RMS_mlp'(h_t)^T (W_1^T u_bar);  a_bar_t = rho W_o^T h_bar
+ *     and query t's own pass (D_t, the ephemeral pair, q_bar's first term);
+ *   - batched again: x_bar = h_bar + RMS_attn'(x)^T (W_q^T q_bar + W_k^T k'_bar
+ *     + W_v^T v'_bar), every weight gradient as a sum over positions and rows
+ *     of (adjoint of a product's output) x (its input), the gains' gradients.
+ *   x      [N][B][d] (dtype): the forward's input, read
+ *   z      [N][B][d] (dtype): the forward's output as stored, read
+ *   z_bar  [N][B][d] fp32: the output adjoint, read
+ *   x_bar  [N][B][d] fp32: the input adjoint, written
+ *   grads: written (overwritten, not accumulated)
+ *   workspace: at least rt_layer_backward_workspace_bytes(desc), 256-byte aligned.
+ * bf16 layers keep adjoints in fp32; a product reads them rounded to bf16 and
+ * accumulates in fp32. Roundings of the forward's stored values are taken as
+ * the identity (their derivative is not defined). Supported: the RT layer
+ * with the blocked or naive schedule (the same map); not RT_FLAG_TRANSFORMER
+ * or RT_FLAG_QK_NORM (RT_ERR_UNSUPPORTED).
+ */
+rt_status rt_layer_backward(const rt_layer_desc* desc, const rt_layer_weights* w, const void* x, const void* z,
+                            const float* z_bar, float* x_bar, const rt_layer_grads* grads,
+                            void* workspace, size_t workspace_bytes, rt_stream_t stream);
+
+/*
  * rt_layer_decode_workspace_bytes -- device workspace of rt_layer_decode_step
  * (independent of seq_len and n_past), or 0 for an invalid descriptor.
  */

@@ -34,6 +34,7 @@ from __future__ import annotations
 import math
 
 import numpy as np
+from scipy.special import erf as _erf
 
 
 def _rms_fwd(x, g, eps):
@@ -53,14 +54,12 @@ def _rms_bwd(x, g, ybar, eps):
 
 
 def _gelu(u):
-    erf = np.vectorize(math.erf)
-    return 0.5 * u * (1.0 + erf(u / math.sqrt(2.0)))
+    return 0.5 * u * (1.0 + _erf(u / math.sqrt(2.0)))
 
 
 def _gelu_grad(u):
     """d/du of u Phi(u): Phi(u) + u phi(u)."""
-    erf = np.vectorize(math.erf)
-    return 0.5 * (1.0 + erf(u / math.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
+    return 0.5 * (1.0 + _erf(u / math.sqrt(2.0))) + u * np.exp(-0.5 * u * u) / math.sqrt(2.0 * math.pi)
 
 
 def layer_backward(x, weights: dict, z_bar, *, n_heads: int, softmax_scale: float, residual_scale: float = 1.0,

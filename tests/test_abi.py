@@ -232,3 +232,33 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="missing"):
         mod.load()
     importlib.reload(rt)
+
+
+def test_layer_backward_validates_its_arguments(lib):
+    d = _layer()
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    G = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    need = rt.rt_layer_backward_workspace_bytes(d)
+    assert need > rt.rt_layer_workspace_bytes(d)
+    # the naive schedule is the same layer map; the Transformer layer and the query/key norm are not covered
+    assert rt.rt_layer_backward_workspace_bytes(_layer(flags=rt.RT_FLAG_NAIVE_SCHEDULE)) == need
+    for flags in (rt.RT_FLAG_TRANSFORMER, rt.RT_FLAG_QK_NORM):
+        assert rt.rt_layer_backward_workspace_bytes(_layer(flags=flags)) == 0
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_layer_backward(_layer(flags=flags), W, FAKE, FAKE, FAKE, FAKE, G, FAKE, need, stream=0)
+        assert e.value.status == 2
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(d, W, FAKE, FAKE, FAKE, FAKE, G, FAKE, need - 1, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(d, W, FAKE, FAKE, None, FAKE, G, FAKE, need, stream=0)
+    assert "z_bar is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(d, W, FAKE, FAKE, FAKE, FAKE, dict(G, w_2=None), FAKE, need, stream=0)
+    assert "grads->w_2 is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(d, W, FAKE, FAKE, FAKE, FAKE, dict(G, g_mlp=FAKE + 2), FAKE, need, stream=0)
+    assert "gain gradients" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(d, W, FAKE, FAKE, FAKE, FAKE, G, FAKE + 16, need, stream=0)
+    assert "256-byte" in str(e.value)
