@@ -405,7 +405,6 @@ struct BLayout {
     size_t rz, rh, rx;                     // [NB] fp32: 1/rms of z, h, x
     size_t pkv;                            // [B][2d] dtype: k_bar|v_bar of one position
     size_t zt;                             // [B][d] fp32: z_bar(total) of one position
-    size_t gb;                             // [B][F] fp32: W_2^T adjoint of one position
     size_t qkvb, kvb;                      // [NB][3d], [NB][2d] dtype: adjoints as product operands
     size_t gpart;                          // gain-gradient partial sums
     size_t total;
@@ -441,7 +440,6 @@ BLayout blayout_of(const rt_layer_desc* d) {
     L.rz = take(NB * 4); L.rh = take(NB * 4); L.rx = take(NB * 4);
     L.pkv = take(B * 2 * D * es);
     L.zt = take(B * D * 4);
-    L.gb = take(B * F * 4);
     L.qkvb = take(NB * 3 * D * es);
     L.kvb = take(NB * 2 * D * es);
     L.gpart = take((size_t)rt::gain_grad_blocks((int64_t)NB) * D * 4);
@@ -547,10 +545,13 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
         RT_TRY(run.check(launch_rms_bwd(dt, dt, (const char*)z + j * rowsD * es, uzb, w->g_attn, eps,
                                         z_bar + j * rowsD, f32(L.zt), zbs, rho, f32(L.rz) + (int64_t)j * B, B, D, s),
                          "RMS_attn adjoint of z"));
-        RT_TRY(plain(zbs, D, at(L.w2T), F, D, f32(L.gb), "W_2^T product"));
         void* ub = base + L.ubar + j * rowsF * es;
-        RT_TRY(run.check(launch_gelu_bwd(dt, f32(L.gb), base + L.u + j * rowsF * es, ub, (int64_t)rowsF, s),
-                         "GELU adjoint"));
+        {   // u_bar = (W_2^T rho z_bar) * GELU'(u_j)
+            GemmArgs g2{};
+            g2.A = zbs; g2.lda = D; g2.W[0] = at(L.w2T); g2.C[0] = ub; g2.ldc = F; g2.seg_n = F;
+            g2.R = base + L.u + j * rowsF * es; g2.ldr = F; g2.M = B; g2.N = F; g2.K = D;
+            RT_TRY(run.check(launch_gemm(dt, GemmKind::W2_BWD, g2, s), "W_2^T product and GELU adjoint"));
+        }
         float* mb = f32(L.mbar) + j * rowsD;
         RT_TRY(plain(ub, F, at(L.w1T), D, F, mb, "W_1^T product"));
         void* hbs = base + L.hbs + j * rowsD * es;

@@ -34,12 +34,18 @@ __device__ __forceinline__ float erf_as(float u) {
 }
 // GELU with the Gaussian CDF: x/2 (1 + erf(x/sqrt 2)).
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erf_as(x * 0.70710678118654752f)); }
+// Its derivative: Phi(x) + x phi(x).
+__device__ __forceinline__ float gelu_erf_grad(float x) {
+    return 0.5f * (1.0f + erf_as(x * 0.70710678118654752f)) +
+           x * __builtin_amdgcn_exp2f(-0.5f * x * x * 1.4426950408889634f) * 0.39894228040143268f;
+}
 
 template <int FLAGS, typename TR, typename TC>
 __device__ __forceinline__ void epilogue_store(const GemmArgs& g, TC* C, int64_t row, int64_t col, float v,
                                                float rstd) {
     if (FLAGS & EPI_RMS) v *= rstd;
     if (FLAGS & EPI_GELU) v = gelu_erf(v);
+    if (FLAGS & EPI_DGELU) v *= gelu_erf_grad(to_f32(((const TR*)g.R)[row * g.ldr + col]));
     if (FLAGS & EPI_RESID) v = to_f32(((const TR*)g.R)[row * g.ldr + col]) + g.rscale * v;
     C[row * g.ldc + (col % g.seg_n)] = from_f32<TC>(v);
 }
@@ -441,6 +447,14 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = gelu_erf(v[e]);
         }
+        if constexpr ((FLAGS & EPI_DGELU) != 0) {
+            if (ok) {
+                float pre[8];
+                load8((const TR*)g.R + row * g.ldr + col, pre);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] *= gelu_erf_grad(pre[e]);
+            }
+        }
         if constexpr ((FLAGS & EPI_QKNORM) != 0) {
             // per-head RMS (query/key norm): a head's head_dim/8 runs sit in as many
             // consecutive lanes (BN is a multiple of head_dim); seg is uniform per workgroup
@@ -611,6 +625,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
                 return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(g, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
             break;
+        case GemmKind::W2_BWD:
+            if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(g, s);
+            break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
                 if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(g, s);
@@ -627,7 +644,7 @@ static int k_groups(GemmKind kind, const GemmArgs& g) {
     if (g.M >= 4096) return 1;
     int ks = kind == GemmKind::W2 ? 4
              : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2
-             : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : 1;
+             : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : kind == GemmKind::W2_BWD ? 2 : 1;
     const int kt = g.K / 64;
     while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
     return ks;
@@ -672,6 +689,7 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
             case GemmKind::KV_UPDATE: return hipErrorInvalidValue;  // bf16 layers only
             case GemmKind::W1_PRE: e = run_f32<float, EPI_RMS>(g, s); break;
             case GemmKind::PLAIN: e = run_f32<float, 0>(g, s); break;
+            case GemmKind::W2_BWD: e = run_f32<float, EPI_DGELU>(g, s); break;
         }
         if (e != hipSuccess || !g.qkn_mask) return e;
         return qk_norm_f32(g, s);

@@ -10,7 +10,8 @@
 //
 // RMS(x) = g x / r with r = sqrt(mean(x^2) + eps) has the adjoint
 //   x_bar = g y_bar / r - x sum(g y_bar x) / (d r^3),   g_bar += y_bar x / r.
-// GELU(u) = u Phi(u) has the derivative Phi(u) + u phi(u).
+// The GELU's derivative Phi(u) + u phi(u) is applied in the W_2^T product's
+// epilogue (gemm.hip).
 #include <rocblas/rocblas.h>
 
 #include "rt_device.h"
@@ -121,17 +122,6 @@ __global__ __launch_bounds__(256) void rms_apply_kernel(const TX* x, const float
     for (int c = threadIdx.x; c < D; c += 256) out[row * D + c] = cvt<TO>((g ? g[c] : 1.f) * ld1(xr + c) * rinv);
 }
 
-__device__ __forceinline__ float gelu_d(float u) {
-    return 0.5f * (1.0f + erff(u * 0.70710678118654752f)) + u * expf(-0.5f * u * u) * 0.39894228040143268f;
-}
-
-// out = gbar * GELU'(u), elementwise.
-template <typename T>
-__global__ __launch_bounds__(256) void gelu_bwd_kernel(const float* gbar, const T* u, T* out, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        out[i] = cvt<T>(gbar[i] * gelu_d(ld1(u + i)));
-}
-
 // u = GELU(u) in place.
 template <typename T>
 __global__ __launch_bounds__(256) void gelu_inplace_kernel(T* u, int64_t n) {
@@ -238,16 +228,6 @@ hipError_t launch_rms_apply(rt_dtype x_dt, rt_dtype out_dt, const void* x, const
     else
         hipLaunchKernelGGL((rms_apply_kernel<float, float>), grid, block, 0, s, (const float*)x, g, eps, (float*)out,
                            D);
-    return hipGetLastError();
-}
-
-hipError_t launch_gelu_bwd(rt_dtype dt, const float* gbar, const void* u, void* out, int64_t n, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    if (dt == RT_BF16)
-        hipLaunchKernelGGL(gelu_bwd_kernel<bf16>, grid_for(n), dim3(256), 0, s, gbar, (const bf16*)u, (bf16*)out, n);
-    else
-        hipLaunchKernelGGL(gelu_bwd_kernel<float>, grid_for(n), dim3(256), 0, s, gbar, (const float*)u, (float*)out,
-                           n);
     return hipGetLastError();
 }
 

@@ -77,6 +77,7 @@ enum : int {
     EPI_PAIRKV = 128,   // tile n holds columns n*BN/2.. of segment 0 (left half) and of segment 1 (right)
     EPI_UPDATE = 256,   // (with EPI_PAIRKV, bf16, head_dim 64) then run upd, a small blocked step whose
                         // newest key/value row is this product's output (see gemm.hip)
+    EPI_DGELU = 512,    // multiply by GELU'(R[row][col]) (the backward through the MLP's activation)
 };
 struct GemmArgs {
     const void* A;      // [M][lda]
@@ -113,6 +114,7 @@ enum class GemmKind {
     KV_UPDATE,// KV (bf16, head_dim 64), then the small blocked step g.upd fused into the same launch
     W1_PRE,   // A = h (bf16 copy with RMS partials, or fp32), RMS, C = W_1 RMS(h) before the GELU (T)
     PLAIN,    // C (fp32) = A (T) * W^T, no epilogue (the backward's adjoint products)
+    W2_BWD,   // C (T) = (A * W^T) * GELU'(R), R = the MLP's pre-activation (T); per-position rows only
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
 
@@ -131,12 +133,10 @@ hipError_t launch_rms_bwd(rt_dtype x_dt, rt_dtype out2_dt, const void* x, const 
 // out = g x / rms(x) per row, in out_dt.
 hipError_t launch_rms_apply(rt_dtype x_dt, rt_dtype out_dt, const void* x, const float* g, float eps, void* out,
                             int64_t rows, int D, hipStream_t s);
-// out = gbar * GELU'(u) (u, out in dt), elementwise over n.
-hipError_t launch_gelu_bwd(rt_dtype dt, const float* gbar, const void* u, void* out, int64_t n, hipStream_t s);
 // u = GELU(u) in place.
 hipError_t launch_gelu_inplace(rt_dtype dt, void* u, int64_t n, hipStream_t s);
 // Gain gradient: out[c] (+)= sum_r y_bar[r][c] x[r][c] rinv[r]; part holds gain_grad_blocks(rows) * D floats.
-constexpr int kGainRowsPerBlock = 256;
+constexpr int kGainRowsPerBlock = 2048;
 int64_t gain_grad_blocks(int64_t rows);
 hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, const float* rinv, int64_t rows, int D,
                             float* part, float* out, int accumulate, hipStream_t s);
