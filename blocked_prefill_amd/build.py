@@ -22,6 +22,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # accumulation registers would cost a copy per score plus occupancy.
 EXTRA = {
     "update.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 # the host pass warns that it does not know the packed-fp32 feature; that is harmless
 NOISE = "is not a recognized feature for this target"

@@ -184,6 +184,12 @@ __global__ __launch_bounds__(256) void bwd_step_kernel(BackwardArgs b, int32_t k
 
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Item of workgroup i when the grid divides by 8: XCD i % 8 gets items
+// (i % 8) * (grid / 8) + 0, 1, ... in dispatch order (a contiguous range of pairs).
+__device__ __forceinline__ int64_t xcd_item(int64_t i, int64_t grid) {
+    return (grid & 7) == 0 ? (i & 7) * (grid >> 3) + (i >> 3) : i;
+}
+
 // Query side: a wave owns 32 queries (columns). Per chunk of 32 keys:
 //   S^T = K Q^T, dP^T = V a_bar^T (A = K, V rows in LDS; B = this wave's q, a_bar)
 //   P^T = 2^(sigma2 S^T - lse), dS^T = P^T (dP^T - delta)
@@ -198,8 +204,10 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
     __shared__ __attribute__((aligned(16))) bf16 Kt[DH * STR];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, ql = lane & 31;
-    const int64_t pair = blockIdx.x / nqt;
-    const int qtile = (int)(blockIdx.x % nqt);
+    // each XCD (workgroup i runs on XCD i % 8) takes a contiguous range of (pair, tile) items
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+    const int64_t pair = item / nqt;
+    const int qtile = (int)(item % nqt);
     const int64_t slab = b.P * DH;
     const int wq0 = qtile * 32 * WAVES + wave * 32;
     const bool active = wq0 < nq;
@@ -313,8 +321,9 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
     __shared__ __attribute__((aligned(16))) float Ds[QT];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, kl = lane & 31;
-    const int64_t pair = blockIdx.x / nkt;
-    const int ktile = (int)(blockIdx.x % nkt);
+    const int64_t item = xcd_item(blockIdx.x, gridDim.x);
+    const int64_t pair = item / nkt;
+    const int ktile = (int)(item % nkt);
     const int64_t slab = b.P * DH;
     const int wk0 = ktile * 32 * WAVES + wave * 32;
     const bool active = wk0 < nkv;

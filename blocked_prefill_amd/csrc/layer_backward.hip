@@ -27,16 +27,6 @@ __device__ __forceinline__ float ld1(const T* p) { return (float)*p; }
 template <typename T>
 __device__ __forceinline__ T cvt(float v) { return (T)v; }
 
-// Sum over a 256-thread workgroup (4 waves); every thread gets the result.
-__device__ __forceinline__ float block_sum256(float v, float* red) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();  // red is free (a previous call's readers are done)
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    return red[0] + red[1] + red[2] + red[3];
-}
-
 // dst[c][col0 + r] = src[r][c] for src [rows][cols] (32x32 tiles through LDS).
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* src, int64_t rows, int64_t cols, T* dst, int64_t ldd,
@@ -76,50 +66,76 @@ __global__ __launch_bounds__(256) void pack_kernel(T* dst, int64_t ldd, const fl
     }
 }
 
-// One workgroup per row: the adjoint of x for y = g x / r given y_bar,
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// One wave per row, 8 consecutive columns per lane and step (D % 8 == 0): the
+// adjoint of x for y = g x / r given y_bar,
 //   out = base + g y_bar / r - x sum(g y_bar x) / (D r^3),
-// and optionally out2 = scale2 * out in T, rinv_out[row] = 1 / r.
+// and optionally out2 = scale2 * out in TO, rinv_out[row] = 1 / r.
 template <typename TX, typename TO>
-__global__ __launch_bounds__(256) void rms_bwd_kernel(const TX* x, const float* ybar, const float* g, float eps,
-                                                      const float* base, float* out, TO* out2, float scale2,
-                                                      float* rinv_out, int D) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(64) void rms_bwd_kernel(const TX* x, const float* ybar, const float* g, float eps,
+                                                     const float* base, float* out, TO* out2, float scale2,
+                                                     float* rinv_out, int D) {
     const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x;
     const TX* xr = x + row * D;
     const float* yr = ybar + row * D;
     float ss = 0.f, sg = 0.f;
-    for (int c = threadIdx.x; c < D; c += 256) {
-        const float xv = ld1(xr + c), gv = g ? g[c] : 1.f;
-        ss += xv * xv;
-        sg += gv * yr[c] * xv;
+    for (int c = lane * 8; c < D; c += 512) {
+        float xv[8], yv[8];
+        load8(xr + c, xv);
+        load8(yr + c, yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            ss += xv[e] * xv[e];
+            sg += (g ? g[c + e] : 1.f) * yv[e] * xv[e];
+        }
     }
-    ss = block_sum256(ss, red);
-    sg = block_sum256(sg, red);
+    ss = wave_sum(ss);
+    sg = wave_sum(sg);
     const float rinv = rsqrtf(ss / (float)D + eps);
     const float coef = sg * rinv * rinv * rinv / (float)D;
-    for (int c = threadIdx.x; c < D; c += 256) {
-        const float xv = ld1(xr + c), gv = g ? g[c] : 1.f;
-        const float o = (base ? base[row * D + c] : 0.f) + gv * yr[c] * rinv - xv * coef;
-        out[row * D + c] = o;
-        if (out2) out2[row * D + c] = cvt<TO>(scale2 * o);
+    for (int c = lane * 8; c < D; c += 512) {
+        float xv[8], yv[8], bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, o[8];
+        load8(xr + c, xv);
+        load8(yr + c, yv);
+        if (base) load8(base + row * D + c, bv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = bv[e] + (g ? g[c + e] : 1.f) * yv[e] * rinv - xv[e] * coef;
+        store8(out + row * D + c, o);
+        if (out2) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= scale2;
+            store8(out2 + row * D + c, o);
+        }
     }
-    if (rinv_out && threadIdx.x == 0) rinv_out[row] = rinv;
+    if (rinv_out && lane == 0) rinv_out[row] = rinv;
 }
 
-// One workgroup per row: out = g x / r in T (the normalised input of a product).
+// One wave per row: out = g x / r in TO (the normalised input of a product).
 template <typename TX, typename TO>
-__global__ __launch_bounds__(256) void rms_apply_kernel(const TX* x, const float* g, float eps, TO* out, int D) {
-    __shared__ float red[4];
+__global__ __launch_bounds__(64) void rms_apply_kernel(const TX* x, const float* g, float eps, TO* out, int D) {
     const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x;
     const TX* xr = x + row * D;
     float ss = 0.f;
-    for (int c = threadIdx.x; c < D; c += 256) {
-        const float xv = ld1(xr + c);
-        ss += xv * xv;
+    for (int c = lane * 8; c < D; c += 512) {
+        float xv[8];
+        load8(xr + c, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += xv[e] * xv[e];
     }
-    ss = block_sum256(ss, red);
-    const float rinv = rsqrtf(ss / (float)D + eps);
-    for (int c = threadIdx.x; c < D; c += 256) out[row * D + c] = cvt<TO>((g ? g[c] : 1.f) * ld1(xr + c) * rinv);
+    const float rinv = rsqrtf(wave_sum(ss) / (float)D + eps);
+    for (int c = lane * 8; c < D; c += 512) {
+        float xv[8];
+        load8(xr + c, xv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] *= (g ? g[c + e] : 1.f) * rinv;
+        store8(out + row * D + c, xv);
+    }
 }
 
 // u = GELU(u) in place.
@@ -144,12 +160,25 @@ __global__ __launch_bounds__(256) void gain_part_kernel(const float* ybar, const
     }
 }
 
-// Second level: out[c] (+)= sum over blocks of part[blk][c], in block order.
-__global__ __launch_bounds__(256) void gain_sum_kernel(const float* part, int nblk, int D, float* out, int accumulate) {
+// Second level: part2[g][c] = sum of part[blk][c] over the blocks of group g
+// (groups of kGainGroup blocks, in block order).
+__global__ __launch_bounds__(256) void gain_fold_kernel(const float* part, int64_t nblk, int D, float* part2) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= D) return;
+    const int64_t b0 = (int64_t)blockIdx.y * kGainGroup;
+    const int64_t b1 = b0 + kGainGroup < nblk ? b0 + kGainGroup : nblk;
+    float acc = 0.f;
+    for (int64_t b = b0; b < b1; ++b) acc += part[b * D + c];
+    part2[(int64_t)blockIdx.y * D + c] = acc;
+}
+
+// Last level: out[c] (+)= sum over groups of part2[g][c], in group order.
+__global__ __launch_bounds__(256) void gain_sum_kernel(const float* part2, int ngroups, int D, float* out,
+                                                       int accumulate) {
     const int c = blockIdx.x * 256 + threadIdx.x;
     if (c >= D) return;
     float acc = 0.f;
-    for (int b = 0; b < nblk; ++b) acc += part[(int64_t)b * D + c];
+    for (int g = 0; g < ngroups; ++g) acc += part2[(int64_t)g * D + c];
     out[c] = accumulate ? out[c] + acc : acc;
 }
 
@@ -197,8 +226,8 @@ hipError_t launch_rms_bwd(rt_dtype x_dt, rt_dtype out2_dt, const void* x, const 
                           float eps, const float* base, float* out, void* out2, float scale2, float* rinv_out,
                           int64_t rows, int D, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (rows >= (1LL << 24)) return hipErrorInvalidConfiguration;  // rows * 256 work-items < 2^32
-    const dim3 grid((uint32_t)rows), block(256);
+    if (rows >= (1LL << 26) || D % 8) return hipErrorInvalidConfiguration;  // rows * 64 work-items < 2^32
+    const dim3 grid((uint32_t)rows), block(64);
     if (x_dt == RT_BF16 && out2_dt == RT_BF16)
         hipLaunchKernelGGL((rms_bwd_kernel<bf16, bf16>), grid, block, 0, s, (const bf16*)x, ybar, g, eps, base, out,
                            (bf16*)out2, scale2, rinv_out, D);
@@ -217,8 +246,8 @@ hipError_t launch_rms_bwd(rt_dtype x_dt, rt_dtype out2_dt, const void* x, const 
 hipError_t launch_rms_apply(rt_dtype x_dt, rt_dtype out_dt, const void* x, const float* g, float eps, void* out,
                             int64_t rows, int D, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
-    if (rows >= (1LL << 24)) return hipErrorInvalidConfiguration;  // rows * 256 work-items < 2^32
-    const dim3 grid((uint32_t)rows), block(256);
+    if (rows >= (1LL << 26) || D % 8) return hipErrorInvalidConfiguration;  // rows * 64 work-items < 2^32
+    const dim3 grid((uint32_t)rows), block(64);
     if (x_dt == RT_BF16 && out_dt == RT_BF16)
         hipLaunchKernelGGL((rms_apply_kernel<bf16, bf16>), grid, block, 0, s, (const bf16*)x, g, eps, (bf16*)out, D);
     else if (x_dt == RT_F32 && out_dt == RT_BF16)
@@ -240,11 +269,14 @@ hipError_t launch_gelu_inplace(rt_dtype dt, void* u, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-int64_t gain_grad_blocks(int64_t rows) { return (rows + kGainRowsPerBlock - 1) / kGainRowsPerBlock; }
+int64_t gain_grad_blocks(int64_t rows) {
+    const int64_t nblk = (rows + kGainRowsPerBlock - 1) / kGainRowsPerBlock;
+    return nblk + (nblk + kGainGroup - 1) / kGainGroup;  // first-level blocks + second-level groups
+}
 
 hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, const float* rinv, int64_t rows, int D,
                             float* part, float* out, int accumulate, hipStream_t s) {
-    const int64_t nblk = gain_grad_blocks(rows);
+    const int64_t nblk = (rows + kGainRowsPerBlock - 1) / kGainRowsPerBlock;
     if (nblk <= 0 || nblk >= (1LL << 24)) return nblk <= 0 ? hipSuccess : hipErrorInvalidConfiguration;
     if (x_dt == RT_BF16)
         hipLaunchKernelGGL(gain_part_kernel<bf16>, dim3((uint32_t)nblk), dim3(256), 0, s, ybar, (const bf16*)x, rinv,
@@ -254,8 +286,14 @@ hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, con
                            rinv, rows, D, kGainRowsPerBlock, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gain_sum_kernel, dim3((uint32_t)((D + 255) / 256)), dim3(256), 0, s, part, (int)nblk, D, out,
-                       accumulate);
+    const int64_t ngroups = (nblk + kGainGroup - 1) / kGainGroup;
+    float* part2 = part + nblk * D;  // (the caller's buffer holds both levels)
+    hipLaunchKernelGGL(gain_fold_kernel, dim3((uint32_t)((D + 255) / 256), (uint32_t)ngroups), dim3(256), 0, s, part,
+                       nblk, D, part2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gain_sum_kernel, dim3((uint32_t)((D + 255) / 256)), dim3(256), 0, s, part2, (int)ngroups, D,
+                       out, accumulate);
     return hipGetLastError();
 }
 

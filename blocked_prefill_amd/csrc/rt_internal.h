@@ -136,7 +136,8 @@ hipError_t launch_rms_apply(rt_dtype x_dt, rt_dtype out_dt, const void* x, const
 // u = GELU(u) in place.
 hipError_t launch_gelu_inplace(rt_dtype dt, void* u, int64_t n, hipStream_t s);
 // Gain gradient: out[c] (+)= sum_r y_bar[r][c] x[r][c] rinv[r]; part holds gain_grad_blocks(rows) * D floats.
-constexpr int kGainRowsPerBlock = 2048;
+constexpr int kGainRowsPerBlock = 256;  // rows per first-level block
+constexpr int kGainGroup = 64;          // first-level blocks per second-level sum
 int64_t gain_grad_blocks(int64_t rows);
 hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, const float* rinv, int64_t rows, int D,
                             float* part, float* out, int accumulate, hipStream_t s);
