@@ -99,6 +99,7 @@ struct Layout {
     size_t hb;            // [rows][d] bf16: h rounded, the MLP's first operand (bf16 layers)
     size_t hss, zss;      // [rows][d/32] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
     size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
+    size_t xss;           // [N*B][4] fp32: quarter-row sums of x^2 (bf16 layers: the up-front RMS)
     size_t total;
 };
 
@@ -134,6 +135,7 @@ Layout layout_of(const rt_layer_desc* d, Mode mode) {
     L.wk = take(D * D * es);
     L.wv = take(D * D * es);
     L.w1 = take(F * D * es);
+    L.xss = take(N * B * 16);
     L.total = off;
     return L;
 }
@@ -203,10 +205,16 @@ rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* 
 // q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x (with the query/key
 // norm on q and k' when the layer has it).
 rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, const void* x,
-                      int64_t rows, void* q, void* ke, void* ve, Launcher& run) {
+                      int64_t rows, void* q, void* ke, void* ve, float* xss, Launcher& run) {
     using namespace rt;
     const int32_t D = d->d_model;
     GemmArgs gq{};
+    if (d->attn.dtype == RT_BF16) {
+        // the rows' sums of squares in a pass of their own: summing them inside the
+        // product's K loop (on the waves holding A) measured 15 % slower at N*B rows
+        RT_TRY(run.check(launch_row_sumsq(RT_BF16, x, rows, D, xss, run.s), "row sums of squares"));
+        gq.rss_in = xss; gq.n_parts = 4;
+    }
     gq.A = x; gq.lda = D;
     gq.W[0] = p.wq; gq.W[1] = p.wk; gq.W[2] = p.wv;
     gq.C[0] = q; gq.C[1] = ke; gq.C[2] = ve;
@@ -282,7 +290,7 @@ rt_status enqueue_transformer(const rt_layer_desc* d, const rt_layer_weights* w,
     char* base = (char*)ws;
     Projections p;
     RT_TRY(enqueue_fold(d, w, base, L, run, &p));
-    RT_TRY(enqueue_qkv(d, w, p, x, rows, base + L.q, kc, vc, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, rows, base + L.q, kc, vc, (float*)(base + L.xss), run));
     UpdateArgs u{};
     u.q = base + L.q; u.k = kc; u.v = vc; u.a_out = base + L.a;
     u.P = (int64_t)d->attn.batch * d->attn.n_heads; u.nq = d->attn.seq_len;
@@ -309,7 +317,7 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
     RT_TRY(enqueue_fold(d, w, base, L, run, &p));
 
     // every query and ephemeral pair depends only on the input: one GEMM up front
-    RT_TRY(enqueue_qkv(d, w, p, x, (int64_t)N * B, q, ke, ve, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, (int64_t)N * B, q, ke, ve, (float*)(base + L.xss), run));
 
     UpdateArgs u{};
     u.q = q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = a;
@@ -369,7 +377,7 @@ rt_status enqueue_decode(const rt_layer_desc* d, const rt_layer_weights* w, int3
     // a Transformer's pair of this position is its ephemeral pair: straight into the caches
     void* ke = transformer ? (void*)kt : (void*)(base + L.ke);
     void* ve = transformer ? (void*)vt : (void*)(base + L.ve);
-    RT_TRY(enqueue_qkv(d, w, p, x, B, base + L.q, ke, ve, run));
+    RT_TRY(enqueue_qkv(d, w, p, x, B, base + L.q, ke, ve, (float*)(base + L.xss), run));
     UpdateArgs u{};
     u.q = base + L.q; u.k = kc; u.v = vc; u.k_eph = ke; u.v_eph = ve; u.a_out = base + L.a;
     u.P = (int64_t)B * H; u.sigma2 = d->attn.softmax_scale * kLog2eHost;
@@ -407,6 +415,7 @@ struct BLayout {
     size_t zt;                             // [B][d] fp32: z_bar(total) of one position
     size_t qkvb, kvb;                      // [NB][3d], [NB][2d] dtype: adjoints as product operands
     size_t gpart;                          // gain-gradient partial sums
+    size_t xss;                            // [NB][4] fp32: quarter-row sums of x^2
     size_t total;
 };
 
@@ -443,6 +452,7 @@ BLayout blayout_of(const rt_layer_desc* d) {
     L.qkvb = take(NB * 3 * D * es);
     L.kvb = take(NB * 2 * D * es);
     L.gpart = take((size_t)rt::gain_grad_blocks((int64_t)NB) * D * 4);
+    L.xss = take(NB * 16);
     L.total = off;
     return L;
 }
@@ -479,7 +489,7 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
     RT_TRY(run.check(launch_transpose(dt, w->w_v, D, D, at(L.wqkvT), 3 * D, 2 * D, s), "transpose W_v"));
 
     // ---- recompute, batched over all N*B rows
-    RT_TRY(enqueue_qkv(d, w, p, x, NB, at(L.q), at(L.ke), at(L.ve), run));
+    RT_TRY(enqueue_qkv(d, w, p, x, NB, at(L.q), at(L.ke), at(L.ve), f32(L.xss), run));
     {   // the persistent pairs from the stored outputs
         GemmArgs gk{};
         gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = at(L.kc); gk.C[1] = at(L.vc);

@@ -117,6 +117,9 @@ enum class GemmKind {
     W2_BWD,   // C (T) = (A * W^T) * GELU'(R), R = the MLP's pre-activation (T); per-position rows only
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
+// out[row][0..3] = sums of x[row][c]^2 over the four quarters of the row (D % 32 == 0); a QKV
+// product given them (rss_in, n_parts = 4) takes its RMS from them.
+hipError_t launch_row_sumsq(rt_dtype dt, const void* x, int64_t rows, int D, float* out, hipStream_t s);
 
 // ---- the layer backward's pieces (layer_backward.hip)
 // dst[c][col0 + r] = src[r][c] for src [rows][cols] (dtype dt), dst row stride ldd.

@@ -137,7 +137,8 @@ def test_workspace_bytes(lib):
     D = h * dh
     al = lambda x: (x + 255) // 256 * 256
     want = 3 * al(n * b * D * 2) + 2 * al(n * b * h * 4) + al(n * b * D * 4) + al(b * D * 2) + al(b * D * 4) \
-        + al(b * f * 2) + al(b * D * 2) + 2 * al(D // 32 * b * 4 + 4) + 3 * al(D * D * 2) + al(f * D * 2)
+        + al(b * f * 2) + al(b * D * 2) + 2 * al(D // 32 * b * 4 + 4) + 3 * al(D * D * 2) + al(f * D * 2) \
+        + al(n * b * 16)  # quarter-row sums of x^2 for the up-front projection
     assert rt.rt_layer_workspace_bytes(d) == want
     assert rt.rt_layer_workspace_bytes(_layer(d_model=100)) == 0
     assert rt.rt_layer_workspace_bytes(_layer(d_ff=100)) == 0  # bf16 needs multiples of 128
@@ -148,18 +149,19 @@ def test_workspace_bytes_of_the_other_modes(lib):
     D = h * dh
     al = lambda x: (x + 255) // 256 * 256
     weights = 3 * al(D * D * 2) + al(f * D * 2)
+    xss = lambda rows: al(rows * 16)  # quarter-row sums of x^2 for the up-front projection
 
     def tail(rows):  # a, h, g, hb, hss, zss
         return al(rows * D * 2) + al(rows * D * 4) + al(rows * f * 2) + al(rows * D * 2) \
             + 2 * al(D // 32 * rows * 4 + 4)
     # naive schedule: no online-softmax state
-    naive = 3 * al(n * b * D * 2) + tail(b) + weights
+    naive = 3 * al(n * b * D * 2) + tail(b) + weights + xss(n * b)
     assert rt.rt_layer_workspace_bytes(_layer(flags=rt.RT_FLAG_NAIVE_SCHEDULE)) == naive
     # Transformer: queries only (pairs go to the caches), every buffer over N*B rows
-    tf = al(n * b * D * 2) + tail(n * b) + weights
+    tf = al(n * b * D * 2) + tail(n * b) + weights + xss(n * b)
     assert rt.rt_layer_workspace_bytes(_layer(flags=rt.RT_FLAG_TRANSFORMER)) == tf
     # decode: one position, independent of seq_len and of the flags
-    dec = 3 * al(b * D * 2) + tail(b) + weights
+    dec = 3 * al(b * D * 2) + tail(b) + weights + xss(b)
     for flags in (0, rt.RT_FLAG_TRANSFORMER, rt.RT_FLAG_NAIVE_SCHEDULE):
         assert rt.rt_layer_decode_workspace_bytes(_layer(flags=flags)) == dec
     assert rt.rt_layer_decode_workspace_bytes(_layer(attn=_attn(seq_len=4096))) == dec
