@@ -12,6 +12,8 @@ algorithmic bytes per launch over its average launch duration; that average
 is one layer's 2047 update launches captured as a HIP graph and replayed,
 timed with HIP events on the launch stream around the replays.
 cpu_baseline = the CPU oracle (naive schedule, fp64) on a bounded sample.
+mfma_util = the layer's algorithmic products and update flops over the layer time
+(the metric's MFMA utilisation, at the layer level).
 """
 import argparse
 import json
@@ -619,6 +621,15 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    # the metric's "MFMA util" at the layer level: the layer's algorithmic products (the up-front
+    # projection 6*N*B*d^2, per position 2B(3d^2 + 2dF)) and the update's 4*dh per (query, key) pair
+    # visited by the blocked schedule, over the measured layer time
+    pairs_visited = sum((t & -t) * min(t & -t, N - t) for t in range(1, N))
+    layer_flops = 6.0 * N * B * D * D + N * 2.0 * B * (3 * D * D + 2 * D * F) + 4.0 * dh * B * H * pairs_visited
+    layer_tflops = layer_flops / (ms_per_step / L * 1e-3) / 1e12
+    out["mfma_util"] = {"scope": "whole layer: all products and the update's scores/values, per layer time",
+                        "alg_TFLOP_per_layer": round(layer_flops / 1e12, 3), "achieved_TFLOP_s": round(layer_tflops, 1),
+                        "peak_TFLOP_s": 2500.0, "frac": round(layer_tflops / 2500.0, 4)}
     if update_info:
         out["update"] = update_info
     print(json.dumps(out), flush=True)
