@@ -2,9 +2,12 @@
 
 One step = the forward pass x -> z of the whole 6-layer RT stack at B=512,
 N=2048, d_model=1024 (16 heads x 64), MLP 4096, bf16, over one batch of seeded
-synthetic input resident in HBM: per layer one HIP-graph replay of the whole
-step loop (up-front Q/K'/V' projection, then per position the fused blocked
-update + finalize, output projection, MLP, persistent K/V projection).
+synthetic input resident in HBM: one HIP-graph replay of the stack plan, whose
+layers run as a wavefront (each layer's per-position products share launches
+with the other layers'; per layer and position: the fused blocked update +
+finalize, output projection, MLP, persistent K/V projection; the queries and
+ephemeral pairs projected in chunks). --per-layer replays one graph per layer
+instead, one layer after another.
 
 Prints one JSON line. value = tokens/s of the stack (B*N tokens per step).
 roofline = the blocked-update kernel (the method's core, HBM-bound): its
@@ -427,6 +430,8 @@ def main():
                     help="attention backward of the blocked schedule at B=512, 16x64 heads, N=2048")
     ap.add_argument("--layer-backward", action="store_true",
                     help="the RT layer's backward at B=512, N=2048, d=1024 (one layer)")
+    ap.add_argument("--per-layer", action="store_true",
+                    help="run the stack as one graph per layer, one after another (no layer wavefront)")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
     args = ap.parse_args()
@@ -475,7 +480,8 @@ def main():
 
     attn = rt.AttnDesc(batch=B, seq_len=N, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=scale)
     desc = rt.LayerDesc(attn=attn, d_model=D, d_ff=F, rms_eps=1e-6, residual_scale=1.0, flags=0)
-    ws_bytes = rt.rt_layer_workspace_bytes(desc)
+    layer_ws = rt.rt_layer_workspace_bytes(desc)
+    ws_bytes = layer_ws if args.per_layer else rt.rt_stack_workspace_bytes(desc, L)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     zs = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
     ks = [torch.empty((N, B, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
@@ -505,11 +511,14 @@ def main():
 
     t0 = time.time()
     plans = []
-    for layer in range(L):
-        xin = x if layer == 0 else zs[layer - 1]
-        plans.append(rt.rt_layer_plan_create(desc, weights[layer], xin, zs[layer], ks[layer], vs[layer], ws))
+    if args.per_layer:  # one graph per layer, replayed one after another
+        for layer in range(L):
+            xin = x if layer == 0 else zs[layer - 1]
+            plans.append(rt.rt_layer_plan_create(desc, weights[layer], xin, zs[layer], ks[layer], vs[layer], ws))
+    else:  # the stack's wavefront as one graph
+        plans.append(rt.rt_stack_plan_create(desc, weights, x, zs, ks, vs, ws))
     capture_s = time.time() - t0
-    log(f"captured {L} layer graphs in {capture_s:.2f}s")
+    log(f"captured {len(plans)} graph(s) in {capture_s:.2f}s")
 
     def step():
         for p in plans:
@@ -542,14 +551,15 @@ def main():
     if not args.no_kernel_timing:
         # the last layer's q, k', v' and state are in the workspace, its caches in ks/vs:
         # replay its update sequence (t = 1..N-1), one event pair per launch
-        durs = update_sequence(rt, attn, ws, ks[-1], vs[-1], N, B, H, D, stream, torch)
+        ws_last = ws if args.per_layer else ws[(L - 1) * layer_ws:]  # the last layer's workspace
+        durs = update_sequence(rt, attn, ws_last, ks[-1], vs[-1], N, B, H, D, stream, torch)
         # the roofline's average launch duration: the same 2047 launches captured as one HIP
         # graph and replayed back to back, two events on the launch stream around the replays
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
-                update_sequence(rt, attn, ws, ks[-1], vs[-1], N, B, H, D, cap, None, sync=False)
+                update_sequence(rt, attn, ws_last, ks[-1], vs[-1], N, B, H, D, cap, None, sync=False)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -617,6 +627,8 @@ def main():
                                f"{H} heads x {dh}, MLP {F} GELU",
                    "batch": B, "seq_len": N, "layers": L, "ms_per_layer": round(ms_per_step / L, 3),
                    "tokens_per_s_per_layer": round(tokens_per_s * L, 1), "graph_capture_s": round(capture_s, 2),
+                   "schedule": ("layer by layer, one graph each" if args.per_layer else
+                                "layer wavefront, one graph (rt_stack_plan_create)"),
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -16,6 +16,7 @@ __all__ = [
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
     "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
     "rt_layer_backward_workspace_bytes", "rt_layer_backward", "LayerGrads", "rt_last_error", "EXPORTED",
+    "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create",
     "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
 ]
 
@@ -24,7 +25,8 @@ RT_FLAG_DEBUG_SYNC = 1
 RT_FLAG_NAIVE_SCHEDULE = 2
 RT_FLAG_TRANSFORMER = 4
 RT_FLAG_QK_NORM = 8
-_STATUS = {0: "RT_OK", 1: "RT_ERR_INVALID_ARG", 2: "RT_ERR_UNSUPPORTED", 3: "RT_ERR_WORKSPACE", 4: "RT_ERR_HIP"}
+_STATUS = {0: "RT_OK", 1: "RT_ERR_INVALID_ARG", 2: "RT_ERR_UNSUPPORTED", 3: "RT_ERR_WORKSPACE", 4: "RT_ERR_HIP",
+           5: "RT_ERR_INTERNAL"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "librt_prefill.so")
@@ -33,7 +35,8 @@ library_path = os.path.join(_HERE, "librt_prefill.so")
 EXPORTED = ["rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_step", "rt_layer_workspace_bytes", "rt_layer_forward",
             "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
             "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
-            "rt_layer_backward_workspace_bytes", "rt_layer_backward", "rt_last_error"]
+            "rt_layer_backward_workspace_bytes", "rt_layer_backward", "rt_last_error",
+            "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create"]
 
 
 class RtError(RuntimeError):
@@ -89,6 +92,12 @@ def load():
             "rt_schedule_step": [_i32, _i32] + [ctypes.POINTER(_i32)] * 4,
             "rt_layer_backward": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _vp, _vp, _vp, _vp,
                                   ctypes.POINTER(LayerGrads), _vp, ctypes.c_size_t, _vp],
+            "rt_stack_forward": [ctypes.POINTER(LayerDesc), _i32, ctypes.POINTER(LayerWeights), _vp,
+                                 ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp, ctypes.c_size_t,
+                                 _vp],
+            "rt_stack_plan_create": [ctypes.POINTER(LayerDesc), _i32, ctypes.POINTER(LayerWeights), _vp,
+                                     ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.POINTER(_vp), _vp,
+                                     ctypes.c_size_t, ctypes.POINTER(_vp)],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -100,6 +109,8 @@ def load():
         L.rt_layer_decode_workspace_bytes.restype = ctypes.c_size_t
         L.rt_layer_backward_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
         L.rt_layer_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.rt_stack_workspace_bytes.argtypes = [ctypes.POINTER(LayerDesc), _i32]
+        L.rt_stack_workspace_bytes.restype = ctypes.c_size_t
         L.rt_layer_plan_destroy.argtypes = [_vp]
         L.rt_layer_plan_destroy.restype = None
         L.rt_last_error.argtypes = []
@@ -239,6 +250,37 @@ def rt_layer_plan_create(desc: LayerDesc, weights, x, z, k_cache, v_cache, works
     h = _vp()
     _check(load().rt_layer_plan_create(ctypes.byref(desc), ctypes.byref(W), _ptr(x), _ptr(z), _ptr(k_cache),
                                        _ptr(v_cache), _ptr(workspace), ws, ctypes.byref(h)))
+    return Plan(h.value, (weights, x, z, k_cache, v_cache, workspace))
+
+
+def rt_stack_workspace_bytes(desc: LayerDesc, n_layers: int) -> int:
+    return int(load().rt_stack_workspace_bytes(ctypes.byref(desc), n_layers))
+
+
+def _stack_args(weights, z, k_cache, v_cache):
+    n = len(weights)
+    if not (len(z) == len(k_cache) == len(v_cache) == n):
+        raise ValueError("weights, z, k_cache and v_cache need one entry per layer")
+    W = (LayerWeights * n)(*[_weights(w) for w in weights])
+    arr = lambda ts: (_vp * n)(*[_ptr(t) for t in ts])  # noqa: E731
+    return n, W, arr(z), arr(k_cache), arr(v_cache)
+
+
+def rt_stack_forward(desc: LayerDesc, weights, x, z, k_cache, v_cache, workspace, workspace_bytes=None,
+                     stream=None):
+    """weights, z, k_cache, v_cache: one entry per layer (z[l] is layer l+1's input)."""
+    ws = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    n, W, Z, K, V = _stack_args(weights, z, k_cache, v_cache)
+    _check(load().rt_stack_forward(ctypes.byref(desc), n, W, _ptr(x), Z, K, V, _ptr(workspace), ws,
+                                   _stream(stream)))
+
+
+def rt_stack_plan_create(desc: LayerDesc, weights, x, z, k_cache, v_cache, workspace, workspace_bytes=None) -> Plan:
+    ws = workspace_bytes if workspace_bytes is not None else workspace.numel() * workspace.element_size()
+    n, W, Z, K, V = _stack_args(weights, z, k_cache, v_cache)
+    h = _vp()
+    _check(load().rt_stack_plan_create(ctypes.byref(desc), n, W, _ptr(x), Z, K, V, _ptr(workspace), ws,
+                                       ctypes.byref(h)))
     return Plan(h.value, (weights, x, z, k_cache, v_cache, workspace))
 
 

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "rt_internal.h"
 
@@ -202,17 +203,15 @@ rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* 
     return RT_OK;
 }
 
-// q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x (with the query/key
-// norm on q and k' when the layer has it).
-rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, const void* x,
-                      int64_t rows, void* q, void* ke, void* ve, float* xss, Launcher& run) {
+// The product q | k' | v' = W_{q,k,v} RMS_attn(x) for `rows` rows of x (with
+// the query/key norm on q and k' when the layer has it); bf16 layers take the
+// RMS from the rows' quarter sums of squares in xss.
+rt::GemmArgs qkv_args(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, const void* x,
+                      int64_t rows, void* q, void* ke, void* ve, const float* xss) {
     using namespace rt;
     const int32_t D = d->d_model;
     GemmArgs gq{};
     if (d->attn.dtype == RT_BF16) {
-        // the rows' sums of squares in a pass of their own: summing them inside the
-        // product's K loop (on the waves holding A) measured 15 % slower at N*B rows
-        RT_TRY(run.check(launch_row_sumsq(RT_BF16, x, rows, D, xss, run.s), "row sums of squares"));
         gq.rss_in = xss; gq.n_parts = 4;
     }
     gq.A = x; gq.lda = D;
@@ -224,12 +223,68 @@ rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const P
         gq.qkn_mask = 3; gq.head_dim = d->attn.head_dim;
         gq.qkn_gain[0] = w->g_q; gq.qkn_gain[1] = w->g_k;
     }
+    return gq;
+}
+
+// q | k' | v' for `rows` rows of x.
+rt_status enqueue_qkv(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, const void* x,
+                      int64_t rows, void* q, void* ke, void* ve, float* xss, Launcher& run) {
+    using namespace rt;
+    if (d->attn.dtype == RT_BF16)
+        // the rows' sums of squares in a pass of their own: summing them inside the
+        // product's K loop (on the waves holding A) measured 15 % slower at N*B rows
+        RT_TRY(run.check(launch_row_sumsq(RT_BF16, x, rows, d->d_model, xss, run.s), "row sums of squares"));
+    const GemmArgs gq = qkv_args(d, w, p, x, rows, q, ke, ve, xss);
     return run.check(launch_gemm(d->attn.dtype, GemmKind::QKV, gq, run.s), "qkv projection");
 }
 
-// Everything after the attention, for `rows` rows:
+// The products after the attention, for `rows` rows:
 //   h = x + rho W_o a;  z = h + rho W_2 GELU(W_1 RMS_mlp(h));
 //   and, when kt is not NULL, the persistent pair k|v = W_{k,v} RMS_attn(z).
+// bf16 layers: W_o also stores h rounded to bf16 (the MLP's operand) and
+// per-row partial sums of h^2; W_2 stores partial sums of z^2 (z as stored).
+// The next product turns those sums into its RMS row scale.
+struct TailArgs {
+    rt::GemmArgs wo, w1, w2, kv;
+};
+
+TailArgs tail_args(const rt_layer_desc* d, const rt_layer_weights* w, const Projections& p, char* base,
+                   const Layout& L, int64_t rows, const void* a, const void* x, void* z, void* kt, void* vt) {
+    using namespace rt;
+    const rt_dtype dt = d->attn.dtype;
+    const int32_t D = d->d_model, F = d->d_ff;
+    void* g = base + L.g;
+    float* h = (float*)(base + L.h);
+    const bool b16 = dt == RT_BF16;
+    const int32_t parts = D / kRowSSTile;
+    TailArgs ta{};
+
+    GemmArgs& go = ta.wo;  // h = x + rho W_o a
+    go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
+    go.R = x; go.ldr = D; go.rscale = d->residual_scale; go.M = rows; go.N = D; go.K = D;
+    if (b16) { go.C2 = base + L.hb; go.rss_out = (float*)(base + L.hss); }
+
+    GemmArgs& g1 = ta.w1;  // g = GELU(W_1 RMS_mlp(h))
+    g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = p.w1; g1.C[0] = g;
+    g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = rows; g1.N = F; g1.K = D;
+    if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
+
+    GemmArgs& g2 = ta.w2;  // z = h + rho W_2 g
+    g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = z; g2.ldc = D; g2.seg_n = D;
+    g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = rows; g2.N = D; g2.K = F;
+    if (b16) g2.rss_out = (float*)(base + L.zss);
+
+    if (kt) {
+        GemmArgs& gk = ta.kv;  // persistent pair from the output z
+        gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = kt; gk.C[1] = vt;
+        gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
+        if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
+        if (d->flags & RT_FLAG_QK_NORM) { gk.qkn_mask = 1; gk.head_dim = d->attn.head_dim; gk.qkn_gain[0] = w->g_k; }
+    }
+    return ta;
+}
+
+// Everything after the attention, for `rows` rows (the products above, in order).
 // fuse (bf16, head_dim 64): a blocked step of 1, 2 or 4 pairs ending at this
 // position, run by the K/V projection's own workgroups once they have stored
 // the pair (one launch fewer on the position's critical path).
@@ -238,45 +293,17 @@ rt_status enqueue_tail(const rt_layer_desc* d, const rt_layer_weights* w, const 
                        Launcher& run, const rt::UpdateArgs* fuse = nullptr) {
     using namespace rt;
     const rt_dtype dt = d->attn.dtype;
-    const int32_t D = d->d_model, F = d->d_ff;
     hipStream_t s = run.s;
-    void* g = base + L.g;
-    float* h = (float*)(base + L.h);
-    // bf16 layers: W_o also stores h rounded to bf16 (the MLP's operand) and
-    // per-row partial sums of h^2; W_2 stores partial sums of z^2 (z as stored).
-    // The next GEMM turns those sums into its RMS row scale.
-    const bool b16 = dt == RT_BF16;
-    const int32_t parts = D / kRowSSTile;
-
-    GemmArgs go{};  // h = x + rho W_o a
-    go.A = a; go.lda = D; go.W[0] = w->w_o; go.C[0] = h; go.ldc = D; go.seg_n = D;
-    go.R = x; go.ldr = D; go.rscale = d->residual_scale; go.M = rows; go.N = D; go.K = D;
-    if (b16) { go.C2 = base + L.hb; go.rss_out = (float*)(base + L.hss); }
-    RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "output projection"));
-
-    GemmArgs g1{};  // g = GELU(W_1 RMS_mlp(h))
-    g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = p.w1; g1.C[0] = g;
-    g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = rows; g1.N = F; g1.K = D;
-    if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
-    RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, g1, s), "mlp up"));
-
-    GemmArgs g2{};  // z = h + rho W_2 g
-    g2.A = g; g2.lda = F; g2.W[0] = w->w_2; g2.C[0] = z; g2.ldc = D; g2.seg_n = D;
-    g2.R = h; g2.ldr = D; g2.rscale = d->residual_scale; g2.M = rows; g2.N = D; g2.K = F;
-    if (b16) g2.rss_out = (float*)(base + L.zss);
-    RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, g2, s), "mlp down"));
-
+    TailArgs ta = tail_args(d, w, p, base, L, rows, a, x, z, kt, vt);
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, ta.wo, s), "output projection"));
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::W1, ta.w1, s), "mlp up"));
+    RT_TRY(run.check(launch_gemm(dt, GemmKind::W2, ta.w2, s), "mlp down"));
     if (!kt) return RT_OK;
-    GemmArgs gk{};  // persistent pair from the output z
-    gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = kt; gk.C[1] = vt;
-    gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
-    if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
-    if (d->flags & RT_FLAG_QK_NORM) { gk.qkn_mask = 1; gk.head_dim = d->attn.head_dim; gk.qkn_gain[0] = w->g_k; }
     if (fuse) {
-        gk.upd = *fuse;
-        return run.check(launch_gemm(dt, GemmKind::KV_UPDATE, gk, s), "persistent kv projection + small step");
+        ta.kv.upd = *fuse;
+        return run.check(launch_gemm(dt, GemmKind::KV_UPDATE, ta.kv, s), "persistent kv projection + small step");
     }
-    return run.check(launch_gemm(dt, GemmKind::KV, gk, s), "persistent kv projection");
+    return run.check(launch_gemm(dt, GemmKind::KV, ta.kv, s), "persistent kv projection");
 }
 
 // The standard Transformer layer: the pairs come from the input, so every
@@ -357,6 +384,175 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
             RT_TRY(run.check(launch_update(dt, dh, u, s), "naive step"));
         }
     }
+    return RT_OK;
+}
+
+// ---------------------------------------------------------------- stacks
+
+// Positions whose queries and ephemeral pairs a stacked layer projects at once:
+// a power of two, N/16 rounded down, at least 8.
+int32_t stack_chunk(int32_t n) {
+    int32_t c = 8;
+    while ((int64_t)c * 2 * 16 <= n) c *= 2;
+    return c;
+}
+
+// A stack of nl layers, layer l's input being layer l-1's output.
+//
+// Blocked layers run as a wavefront: at tick tau, layer l takes position
+// t = tau - l*lag, and the per-position products of all layers at their
+// positions share one launch each (one product at a time leaves most of the
+// chip idle). Layer l >= 1 can only project a query once layer l-1 has made
+// the position's input, so it projects its queries and ephemeral pairs in
+// chunks of C positions, chunk [kC+1, (k+1)C] at position kC (lag = C + 8 >
+// C keeps layer l-1 ahead of the chunk; a multiple of 8 keeps the blocks of
+// 1, 2 and 4 pairs at the same ticks in every layer).
+//
+// The blocked schedule is kept exactly. Step t applies its block to queries
+// t+1..t+b; those not yet projected (only when b >= C, t = kC: rows past
+// t + C) are applied when their chunk is projected, before any later step
+// touches them. Every query thus merges the same blocks in the same order as
+// in the layer-by-layer run; a block of b > C pairs is read once per chunk of
+// its deferred rows instead of once.
+rt_status enqueue_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weights* w, const void* x,
+                        void* const* z, void* const* kc, void* const* vc, void* ws, size_t stride, hipStream_t s,
+                        bool debug) {
+    using namespace rt;
+    const Mode mode = mode_of(d);
+    if (mode != Mode::Blocked || nl == 1) {  // layer after layer
+        for (int32_t l = 0; l < nl; ++l)
+            RT_TRY(enqueue_layer(d, &w[l], l ? z[l - 1] : x, z[l], kc[l], vc[l], (char*)ws + l * stride, s, debug));
+        return RT_OK;
+    }
+    Launcher run{s, debug};
+    const rt_dtype dt = d->attn.dtype;
+    const size_t es = elem_bytes(dt);
+    const int32_t N = d->attn.seq_len, B = d->attn.batch, H = d->attn.n_heads, dh = d->attn.head_dim;
+    const Layout L = layout_of(d, mode);
+    const size_t slab = (size_t)B * d->d_model * es;
+    const int32_t C = stack_chunk(N), lag = C + 8;
+    const bool fuse_small = dt == RT_BF16 && dh == 64;
+
+    struct Deferred {
+        int32_t kv0, nkv, init;  // the block: key rows kv0..kv0+nkv-1 (0-based); its step initialises the rows
+        int32_t r0, r1;          // query positions r0..r1 (1-based) still to receive it
+    };
+    struct Stacked {
+        const rt_layer_weights* w;
+        const char* x;
+        char *z, *kc, *vc, *base;
+        Projections p;
+        UpdateArgs u;
+        int32_t avail;                  // positions 1..avail have their queries and ephemeral pairs
+        std::vector<Deferred> pending;  // in step order
+    };
+    std::vector<Stacked> ly(nl);
+    for (int32_t l = 0; l < nl; ++l) {
+        Stacked& y = ly[l];
+        y.w = &w[l];
+        y.x = (const char*)(l ? z[l - 1] : x);
+        y.z = (char*)z[l];
+        y.kc = (char*)kc[l];
+        y.vc = (char*)vc[l];
+        y.base = (char*)ws + l * stride;
+        RT_TRY(enqueue_fold(d, y.w, y.base, L, run, &y.p));
+        UpdateArgs& u = y.u;
+        u = UpdateArgs{};
+        u.q = y.base + L.q; u.k = y.kc; u.v = y.vc; u.k_eph = y.base + L.ke; u.v_eph = y.base + L.ve;
+        u.a_out = y.base + L.a;
+        u.m = (float*)(y.base + L.m); u.l = (float*)(y.base + L.l); u.o = (float*)(y.base + L.o);
+        u.P = (int64_t)B * H; u.sigma2 = d->attn.softmax_scale * kLog2eHost;
+        y.avail = 0;
+    }
+    auto update = [&](const Stacked& y, int32_t kv0, int32_t nkv, int32_t q0, int32_t nq, bool init, bool fin,
+                      const char* what) {
+        UpdateArgs u = y.u;
+        u.kv0 = kv0; u.nkv = nkv; u.q0 = q0; u.nq = nq; u.init = init; u.fin = fin;
+        return run.check(launch_update(dt, dh, u, s), what);
+    };
+    // queries and ephemeral pairs of positions avail+1..r1, then the deferred
+    // blocks of those positions, oldest step first
+    auto project = [&](Stacked& y, int32_t r1) -> rt_status {
+        const int32_t r0 = y.avail + 1;
+        const size_t at = (size_t)(r0 - 1) * slab;
+        float* xss = (float*)(y.base + L.xss) + (size_t)(r0 - 1) * B * 4;
+        RT_TRY(enqueue_qkv(d, y.w, y.p, y.x + at, (int64_t)(r1 - r0 + 1) * B, y.base + L.q + at,
+                           y.base + L.ke + at, y.base + L.ve + at, xss, run));
+        y.avail = r1;
+        for (Deferred& e : y.pending) {
+            const int32_t a = e.r0 > r0 ? e.r0 : r0, b = e.r1 < r1 ? e.r1 : r1;
+            if (a > b) continue;
+            RT_TRY(update(y, e.kv0, e.nkv, a - 1, b - a + 1, e.init != 0, false, "deferred blocked update"));
+            e.r0 = b + 1;
+        }
+        size_t keep = 0;
+        for (const Deferred& e : y.pending)
+            if (e.r0 <= e.r1) y.pending[keep++] = e;
+        y.pending.resize(keep);
+        return RT_OK;
+    };
+    RT_TRY(project(ly[0], N));  // the first layer's input is given: every position up front
+
+    std::vector<GemmArgs> go, g1, g2, gk, gku;
+    std::vector<int32_t> act;
+    const int64_t ticks = (int64_t)N + (int64_t)(nl - 1) * lag;
+    for (int64_t tau = 1; tau <= ticks; ++tau) {
+        act.clear();
+        for (int32_t l = 0; l < nl; ++l) {
+            const int64_t t = tau - (int64_t)l * lag;
+            if (t >= 1 && t <= N) act.push_back(l);
+        }
+        go.clear(); g1.clear(); g2.clear(); gk.clear(); gku.clear();
+        for (int32_t l : act) {
+            Stacked& y = ly[l];
+            const int32_t t = (int32_t)(tau - (int64_t)l * lag);
+            // position t+1's query is read by this position's step: project its chunk
+            // (layer l-1 has finished positions < t + lag, past the chunk's end)
+            if (y.avail <= t && y.avail < N) {
+                const int32_t r1 = (int64_t)y.avail + C < N ? y.avail + C : N;
+                RT_TRY(project(y, r1));
+            }
+            if (t == 1)  // position 1: empty state, a_1 is its own ephemeral value
+                RT_TRY(update(y, 0, 0, 0, 1, true, true, "finalize position 1"));
+            const size_t at = (size_t)(t - 1) * slab;
+            TailArgs ta = tail_args(d, y.w, y.p, y.base, L, B, y.base + L.a, y.x + at, y.z + at, y.kc + at,
+                                    y.vc + at);
+            go.push_back(ta.wo);
+            g1.push_back(ta.w1);
+            g2.push_back(ta.w2);
+            const int32_t bt = block_of(t);
+            if (fuse_small && t < N && bt <= 4) {
+                UpdateArgs& u = ta.kv.upd;
+                u = y.u;
+                u.kv0 = t - bt; u.nkv = bt; u.q0 = t; u.nq = (bt < N - t) ? bt : N - t;
+                u.init = (bt == t); u.fin = 1;
+                gku.push_back(ta.kv);
+            } else {
+                gk.push_back(ta.kv);
+            }
+        }
+        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::WO, go.data(), (int)go.size(), s), "output projections"));
+        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::W1, g1.data(), (int)g1.size(), s), "mlp up"));
+        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::W2, g2.data(), (int)g2.size(), s), "mlp down"));
+        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV_UPDATE, gku.data(), (int)gku.size(), s),
+                         "persistent kv projections + small steps"));
+        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV, gk.data(), (int)gk.size(), s),
+                         "persistent kv projections"));
+        for (int32_t l : act) {
+            Stacked& y = ly[l];
+            const int32_t t = (int32_t)(tau - (int64_t)l * lag);
+            const int32_t b = block_of(t);
+            if (t == N || (fuse_small && b <= 4)) continue;
+            // blocked step t: its block to queries t+1..t+b, finishing t+1; the
+            // queries not yet projected get it when their chunk is
+            const int32_t r1 = (int64_t)t + b < N ? t + b : N;
+            const int32_t now = r1 < y.avail ? r1 : y.avail;
+            RT_TRY(update(y, t - b, b, t, now - t, b == t, true, "blocked update"));
+            if (r1 > now) y.pending.push_back(Deferred{t - b, b, b == t ? 1 : 0, now + 1, r1});
+        }
+    }
+    for (const Stacked& y : ly)
+        if (!y.pending.empty() || y.avail != N) return fail(RT_ERR_INTERNAL, "the stack schedule left work undone");
     return RT_OK;
 }
 
@@ -633,6 +829,60 @@ struct rt_plan {
     hipGraphExec_t exec = nullptr;
 };
 
+namespace {
+
+constexpr int32_t kMaxStackLayers = 1024;
+
+rt_status check_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weights* w, const void* x, void* const* z,
+                      void* const* kc, void* const* vc, void* ws, size_t ws_bytes) {
+    RT_TRY(check_layer(d));
+    if (nl < 1 || nl > kMaxStackLayers)
+        return fail(RT_ERR_INVALID_ARG, "n_layers=%d outside 1..%d", nl, kMaxStackLayers);
+    if (!w || !z || !kc || !vc) return fail(RT_ERR_INVALID_ARG, "weights, z, k_cache or v_cache array is NULL");
+    for (int32_t l = 0; l < nl; ++l) {
+        const rt_status st = check_layer_ptrs(&w[l], l ? z[l - 1] : x, z[l], kc[l], vc[l], ws);
+        if (st != RT_OK) return fail(st, "layer %d: %s", l, g_last_error.c_str());
+    }
+    const size_t need = (size_t)nl * layout_of(d, mode_of(d)).total;
+    if (ws_bytes < need) return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+    return RT_OK;
+}
+
+// Capture what enqueue puts on a stream into a HIP graph, instantiated.
+template <typename F>
+rt_status capture_plan(F&& enqueue, rt_plan** plan) {
+    hipStream_t cs;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "capture stream");
+    rt_plan* p = new rt_plan();
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        delete p;
+        return hip_fail(e, "hipStreamBeginCapture");
+    }
+    rt_status st = enqueue(cs);
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    (void)hipStreamDestroy(cs);
+    if (st != RT_OK || e != hipSuccess) {
+        if (graph) (void)hipGraphDestroy(graph);
+        delete p;
+        return st != RT_OK ? st : hip_fail(e, "hipStreamEndCapture");
+    }
+    p->graph = graph;
+    e = hipGraphInstantiate(&p->exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) {
+        (void)hipGraphDestroy(graph);
+        delete p;
+        return hip_fail(e, "hipGraphInstantiate");
+    }
+    *plan = p;
+    return RT_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rt_last_error(void) { return g_last_error.c_str(); }
@@ -874,34 +1124,35 @@ rt_status rt_layer_plan_create(const rt_layer_desc* desc, const rt_layer_weights
     const size_t need = layout_of(desc, mode_of(desc)).total;
     if (workspace_bytes < need)
         return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);
-    hipStream_t cs;
-    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-    if (e != hipSuccess) return hip_fail(e, "capture stream");
-    rt_plan* p = new rt_plan();
-    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-    if (e != hipSuccess) {
-        (void)hipStreamDestroy(cs);
-        delete p;
-        return hip_fail(e, "hipStreamBeginCapture");
-    }
-    rt_status st = enqueue_layer(desc, w, x, z, k_cache, v_cache, workspace, cs, false);
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(cs, &graph);
-    (void)hipStreamDestroy(cs);
-    if (st != RT_OK || e != hipSuccess) {
-        if (graph) (void)hipGraphDestroy(graph);
-        delete p;
-        return st != RT_OK ? st : hip_fail(e, "hipStreamEndCapture");
-    }
-    p->graph = graph;
-    e = hipGraphInstantiate(&p->exec, graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-        (void)hipGraphDestroy(graph);
-        delete p;
-        return hip_fail(e, "hipGraphInstantiate");
-    }
-    *plan = p;
-    return RT_OK;
+    return capture_plan([&](hipStream_t cs) { return enqueue_layer(desc, w, x, z, k_cache, v_cache, workspace, cs, false); },
+                        plan);
+}
+
+size_t rt_stack_workspace_bytes(const rt_layer_desc* desc, int32_t n_layers) {
+    if (check_layer(desc) != RT_OK || n_layers < 1 || n_layers > kMaxStackLayers) return 0;
+    return (size_t)n_layers * layout_of(desc, mode_of(desc)).total;
+}
+
+rt_status rt_stack_forward(const rt_layer_desc* desc, int32_t n_layers, const rt_layer_weights* w, const void* x,
+                           void* const* z, void* const* k_cache, void* const* v_cache, void* workspace,
+                           size_t workspace_bytes, rt_stream_t stream) {
+    RT_TRY(check_stack(desc, n_layers, w, x, z, k_cache, v_cache, workspace, workspace_bytes));
+    return enqueue_stack(desc, n_layers, w, x, z, k_cache, v_cache, workspace, layout_of(desc, mode_of(desc)).total,
+                         (hipStream_t)stream, (desc->flags & RT_FLAG_DEBUG_SYNC) != 0);
+}
+
+rt_status rt_stack_plan_create(const rt_layer_desc* desc, int32_t n_layers, const rt_layer_weights* w, const void* x,
+                               void* const* z, void* const* k_cache, void* const* v_cache, void* workspace,
+                               size_t workspace_bytes, rt_plan** plan) {
+    if (!plan) return fail(RT_ERR_INVALID_ARG, "plan is NULL");
+    *plan = nullptr;
+    RT_TRY(check_stack(desc, n_layers, w, x, z, k_cache, v_cache, workspace, workspace_bytes));
+    const size_t stride = layout_of(desc, mode_of(desc)).total;
+    return capture_plan(
+        [&](hipStream_t cs) {
+            return enqueue_stack(desc, n_layers, w, x, z, k_cache, v_cache, workspace, stride, cs, false);
+        },
+        plan);
 }
 
 rt_status rt_layer_plan_launch(rt_plan* plan, rt_stream_t stream) {

@@ -167,8 +167,8 @@ __device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16
 // buffers, and the KS partial tiles are added in LDS before the epilogue. At
 // the per-position shapes (M = batch) this multiplies the waves per tile and
 // divides the serial K-loop length without any cross-workgroup reduction.
-template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
-__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g) {
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS>
+__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
     // MF = 32: v_mfma_f32_32x32x16_bf16 blocks; MF = 16: v_mfma_f32_16x16x32_bf16 blocks
     // (four times as many independent accumulators for the same wave tile).
     static_assert(MF == 32 || MF == 16, "MFMA block");
@@ -523,13 +523,50 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g
     }
 }
 
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g) {
+    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g);
+}
+
+// Several products of the same kind and shape in one launch (blockIdx.z picks
+// the product; row counts may differ, the grid covers the largest): the
+// per-position products of the layers of a stack, which one at a time leave
+// most of the chip idle.
+struct GemmGroup {
+    GemmArgs g[kMaxGemmGroup];
+};
+static_assert(sizeof(GemmGroup) <= 3584, "kernel argument size");
+
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
+__global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_group_kernel(GemmGroup gg) {
+    const GemmArgs& g = gg.g[blockIdx.z];
+    if ((int64_t)blockIdx.y * BM >= g.M) return;  // past this product's rows (the whole workgroup)
+    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g);
+}
+
+// The products of one launch: n argument sets of one kind and shape (n <= kMaxGemmGroup).
+struct GemmSet {
+    const GemmArgs* g;
+    int n;
+    int64_t max_m;
+};
+
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32, int KS = 1>
-static hipError_t run_pipe(const GemmArgs& g, hipStream_t s) {
-    const int64_t row_tiles = (g.M + BM - 1) / BM;
+static hipError_t run_pipe(const GemmSet& gs, hipStream_t s) {
+    const GemmArgs& g = gs.g[0];
+    const int64_t row_tiles = (gs.max_m + BM - 1) / BM;
     if (row_tiles > 65535) return hipErrorInvalidConfiguration;  // grid y limit
-    dim3 grid((uint32_t)(g.N / BN), (uint32_t)row_tiles);
-    hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>), grid, dim3(64 * WM * WN * KS), 0,
-                       s, g);
+    if (gs.n == 1) {
+        dim3 grid((uint32_t)(g.N / BN), (uint32_t)row_tiles);
+        hipLaunchKernelGGL((gemm_pipe_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>), grid,
+                           dim3(64 * WM * WN * KS), 0, s, g);
+    } else {
+        GemmGroup gg{};
+        for (int i = 0; i < gs.n; ++i) gg.g[i] = gs.g[i];
+        dim3 grid((uint32_t)(g.N / BN), (uint32_t)row_tiles, (uint32_t)gs.n);
+        hipLaunchKernelGGL((gemm_pipe_group_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>), grid,
+                           dim3(64 * WM * WN * KS), 0, s, gg);
+    }
     return hipGetLastError();
 }
 
@@ -569,15 +606,21 @@ bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K) {
 }
 
 template <int D, int KS>
-static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s) {
-    const bool big = g.M >= 4096;
+static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s) {
+    const GemmArgs& g = gs.g[0];  // the shape and flags every product of the set shares
+    const bool big = gs.max_m >= 4096;
+    const bool grouped = !big && gs.n >= 2;
     // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
     // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave),
     // with K split over 2 or 4 wave groups where that measured faster (W_2,
     // W_o, W_kv); products over N*B rows (the up-front projection, and every
     // product of the Transformer layer) use 128x128, prefetching 2 K tiles
     // ahead in the tall products with fp32 operands in the epilogue (register
-    // budget: 2 waves per SIMD).
+    // budget: 2 waves per SIMD). Several per-position products in one launch
+    // (the layers of a stack) fill the chip, and larger tiles then win: for six
+    // products of 512 rows, W_1 128x128 46.8 us against 58.8 with the
+    // per-position tile, W_2 128x128 with 2 K groups 45.2 against 77.4, W_o
+    // 64x64 18.9 against 25.6, W_kv 128x128 25.3 against 38.6.
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1) {
@@ -585,63 +628,73 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
                 // partial-sum variant measured 535 us per 65536 rows with 2, 806 with 4
                 if (g.rss_in) {  // row sums of squares given (row_sumsq): RMS from the partials
                     if (g.qkn_mask)
-                        return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(g, s)
-                                   : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(g, s);
-                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(g, s)
-                               : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
+                        return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s)
+                                   : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(gs, s);
+                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
+                               : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
                 }
                 if (g.qkn_mask)
-                    return big ? run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(g, s)
-                               : run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(g, s);
-                return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, 2, 32>(g, s)
-                           : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(g, s);
+                    return big ? run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s)
+                               : run_pipe<bf16, float, EPI_RMS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(gs, s);
+                return big ? run_pipe<bf16, float, EPI_RMS, 128, 128, 2, 2, 2, 32>(gs, s)
+                           : run_pipe<bf16, float, EPI_RMS, 64, 64, 2, 2, D, 16>(gs, s);
             }
             break;
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
             if constexpr (KS == 1) {
-                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(g, s);
+                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
+                if (grouped) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, D, 16>(gs, s);
             }
             if constexpr (KS <= 2)
-                if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+                if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
         case GemmKind::W1:
             if constexpr (KS == 1)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(g, s)
-                           : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(g, s);
+                return big || grouped ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
+                                      : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(gs, s);
             break;
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
             if constexpr (KS == 1) {
-                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(g, s);
+                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
             }
-            if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(g, s);
+            if constexpr (KS == 2) {
+                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32, 2>(gs, s);
+            }
+            if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
         case GemmKind::KV_UPDATE:
             if constexpr (KS <= 2) {
                 if (g.qkn_mask)
                     return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_PAIRKV | EPI_UPDATE | EPI_QKNORM, 32, 128, 1, 4, D,
-                                    16, KS>(g, s);
-                return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_PAIRKV | EPI_UPDATE, 32, 128, 1, 4, D, 16, KS>(g, s);
+                                    16, KS>(gs, s);
+                return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_PAIRKV | EPI_UPDATE, 32, 128, 1, 4, D, 16, KS>(gs, s);
             }
             break;
         case GemmKind::KV:
+            if constexpr (KS == 1) {
+                if (grouped) {
+                    if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s);
+                    return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s);
+                }
+            }
             if constexpr (KS <= 2) {
-                if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16, KS>(g, s);
-                return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(g, s);
+                if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16, KS>(gs, s);
+                return run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16, KS>(gs, s);
             }
             break;
         case GemmKind::W1_PRE:
             if constexpr (KS == 1)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(g, s)
-                           : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(g, s);
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
+                           : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
             break;
         case GemmKind::W2_BWD:
-            if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(g, s);
+            if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(gs, s);
             break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
-                if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(g, s);
+                if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(gs, s);
             }
-            if (!big) return run_pipe<float, float, 0, 64, 64, 2, 2, D, 16, KS>(g, s);
+            if (!big) return run_pipe<float, float, 0, 64, 64, 2, 2, D, 16, KS>(gs, s);
             break;
     }
     return hipErrorInvalidValue;
@@ -649,11 +702,12 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmArgs& g, hipStream_t s)
 
 // K groups per workgroup for a kind and shape: the measured choice when K
 // divides into an even number of 64-wide tiles per group, else fewer.
-static int k_groups(GemmKind kind, const GemmArgs& g) {
-    if (g.M >= 4096) return 1;
+static int k_groups(GemmKind kind, const GemmArgs& g, int64_t max_m, int n) {
+    if (max_m >= 4096) return 1;
     int ks = kind == GemmKind::W2 ? 4
              : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2
              : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : kind == GemmKind::W2_BWD ? 2 : 1;
+    if (n >= 2 && kind != GemmKind::KV_UPDATE) ks = kind == GemmKind::W2 ? 2 : 1;  // several products per launch
     const int kt = g.K / 64;
     while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
     return ks;
@@ -686,34 +740,62 @@ static hipError_t qk_norm_f32(const GemmArgs& g, hipStream_t s) {
     return hipSuccess;
 }
 
+static hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t s) {
+    hipError_t e = hipErrorInvalidValue;
+    switch (kind) {
+        case GemmKind::QKV: e = run_f32<float, EPI_RMS>(g, s); break;
+        case GemmKind::WO: e = run_f32<float, EPI_RESID>(g, s); break;
+        case GemmKind::W1: e = run_f32<float, EPI_RMS | EPI_GELU>(g, s); break;
+        case GemmKind::W2: e = run_f32<float, EPI_RESID>(g, s); break;
+        case GemmKind::KV: e = run_f32<float, EPI_RMS>(g, s); break;
+        case GemmKind::KV_UPDATE: return hipErrorInvalidValue;  // bf16 layers only
+        case GemmKind::W1_PRE: e = run_f32<float, EPI_RMS>(g, s); break;
+        case GemmKind::PLAIN: e = run_f32<float, 0>(g, s); break;
+        case GemmKind::W2_BWD: e = run_f32<float, EPI_DGELU>(g, s); break;
+    }
+    if (e != hipSuccess || !g.qkn_mask) return e;
+    return qk_norm_f32(g, s);
+}
+
+// Products that may share a launch: the same shape and the same epilogue inputs.
+static bool same_shape(const GemmArgs& a, const GemmArgs& b) {
+    return a.N == b.N && a.K == b.K && a.seg_n == b.seg_n && a.n_parts == b.n_parts &&
+           (a.rss_in != nullptr) == (b.rss_in != nullptr) && a.qkn_mask == b.qkn_mask &&
+           a.head_dim == b.head_dim && a.M > 0 && b.M > 0;
+}
+
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s) {
-    if (dt == RT_F32) {
-        hipError_t e = hipErrorInvalidValue;
-        switch (kind) {
-            case GemmKind::QKV: e = run_f32<float, EPI_RMS>(g, s); break;
-            case GemmKind::WO: e = run_f32<float, EPI_RESID>(g, s); break;
-            case GemmKind::W1: e = run_f32<float, EPI_RMS | EPI_GELU>(g, s); break;
-            case GemmKind::W2: e = run_f32<float, EPI_RESID>(g, s); break;
-            case GemmKind::KV: e = run_f32<float, EPI_RMS>(g, s); break;
-            case GemmKind::KV_UPDATE: return hipErrorInvalidValue;  // bf16 layers only
-            case GemmKind::W1_PRE: e = run_f32<float, EPI_RMS>(g, s); break;
-            case GemmKind::PLAIN: e = run_f32<float, 0>(g, s); break;
-            case GemmKind::W2_BWD: e = run_f32<float, EPI_DGELU>(g, s); break;
+    return launch_gemm_group(dt, kind, &g, 1, s);
+}
+
+hipError_t launch_gemm_group(rt_dtype dt, GemmKind kind, const GemmArgs* gs, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    for (int i = 1; i < n; ++i)
+        if (!same_shape(gs[0], gs[i])) return hipErrorInvalidValue;
+    if (dt == RT_F32) {  // one launch per product
+        for (int i = 0; i < n; ++i) {
+            const hipError_t e = launch_gemm_f32(kind, gs[i], s);
+            if (e != hipSuccess) return e;
         }
-        if (e != hipSuccess || !g.qkn_mask) return e;
-        return qk_norm_f32(g, s);
+        return hipSuccess;
     }
     // K is a multiple of 128 (an even number of 64-wide K tiles); each K group
     // prefetches 4 tiles ahead when its tile count divides by 4, else 2
-    if ((g.K / 64) % 2) return hipErrorInvalidValue;
-    const int ks = k_groups(kind, g);
-    const bool d4 = (g.K / 64 / ks) % 4 == 0;
-    switch (ks) {
-        case 1: return d4 ? dispatch_bf16<4, 1>(kind, g, s) : dispatch_bf16<2, 1>(kind, g, s);
-        case 2: return d4 ? dispatch_bf16<4, 2>(kind, g, s) : dispatch_bf16<2, 2>(kind, g, s);
-        case 4: return d4 ? dispatch_bf16<4, 4>(kind, g, s) : dispatch_bf16<2, 4>(kind, g, s);
+    if ((gs[0].K / 64) % 2) return hipErrorInvalidValue;
+    for (int i0 = 0; i0 < n; i0 += kMaxGemmGroup) {
+        GemmSet set{gs + i0, n - i0 < kMaxGemmGroup ? n - i0 : kMaxGemmGroup, 0};
+        for (int i = 0; i < set.n; ++i) set.max_m = set.g[i].M > set.max_m ? set.g[i].M : set.max_m;
+        const int ks = k_groups(kind, set.g[0], set.max_m, set.n);
+        const bool d4 = (set.g[0].K / 64 / ks) % 4 == 0;
+        hipError_t e = hipErrorInvalidValue;
+        switch (ks) {
+            case 1: e = d4 ? dispatch_bf16<4, 1>(kind, set, s) : dispatch_bf16<2, 1>(kind, set, s); break;
+            case 2: e = d4 ? dispatch_bf16<4, 2>(kind, set, s) : dispatch_bf16<2, 2>(kind, set, s); break;
+            case 4: e = d4 ? dispatch_bf16<4, 4>(kind, set, s) : dispatch_bf16<2, 4>(kind, set, s); break;
+        }
+        if (e != hipSuccess) return e;
     }
-    return hipErrorInvalidValue;
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------- row sums of squares

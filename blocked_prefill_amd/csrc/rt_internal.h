@@ -117,6 +117,11 @@ enum class GemmKind {
     W2_BWD,   // C (T) = (A * W^T) * GELU'(R), R = the MLP's pre-activation (T); per-position rows only
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
+// n products of one kind and shape (the same N, K and epilogue inputs; row
+// counts may differ) in as few launches as possible, kMaxGemmGroup per launch
+// (bf16; fp32 products run one launch each).
+constexpr int kMaxGemmGroup = 8;
+hipError_t launch_gemm_group(rt_dtype dt, GemmKind kind, const GemmArgs* gs, int n, hipStream_t s);
 // out[row][0..3] = sums of x[row][c]^2 over the four quarters of the row (D % 32 == 0); a QKV
 // product given them (rss_in, n_parts = 4) takes its RMS from them.
 hipError_t launch_row_sumsq(rt_dtype dt, const void* x, int64_t rows, int D, float* out, hipStream_t s);

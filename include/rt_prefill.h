@@ -52,7 +52,8 @@ typedef enum {
     RT_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, t out of range, misaligned pointer */
     RT_ERR_UNSUPPORTED = 2,  /* valid but not implemented: head_dim not in {32, 64, 128}, odd sizes */
     RT_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than rt_layer_workspace_bytes() */
-    RT_ERR_HIP = 4           /* a HIP runtime call failed; see rt_last_error() */
+    RT_ERR_HIP = 4,          /* a HIP runtime call failed; see rt_last_error() */
+    RT_ERR_INTERNAL = 5      /* an internal consistency check failed (a defect of this library) */
 } rt_status;
 
 typedef enum { RT_F32 = 0, RT_BF16 = 1 } rt_dtype;
@@ -323,6 +324,38 @@ rt_status rt_layer_plan_create(const rt_layer_desc* desc, const rt_layer_weights
                                void* workspace, size_t workspace_bytes, rt_plan** plan);
 rt_status rt_layer_plan_launch(rt_plan* plan, rt_stream_t stream);
 void rt_layer_plan_destroy(rt_plan* plan);
+
+/*
+ * Stacks: n_layers RT layers of one shape, layer l's input being layer
+ * l-1's output (translated paper section 6.1: each layer's stored output z
+ * is the next layer's input), so x -> z[n_layers-1] is the model's forward.
+ *   desc      one descriptor for every layer (shape, dtype, flags)
+ *   w         [n_layers] the layers' weights
+ *   x         [N][B][d] input of layer 0 (dtype), read
+ *   z         [n_layers] outputs [N][B][d] (dtype), written; z[l] is layer l+1's input
+ *   k_cache, v_cache  [n_layers] persistent pairs [N][B][H][dh] of each layer, written
+ *   workspace: at least rt_stack_workspace_bytes(desc, n_layers), 256-byte aligned.
+ * Each layer computes the map of rt_layer_forward, with the same schedule.
+ * Blocked layers run as a wavefront: layer l works on position t while layer
+ * l-1 is C + 8 positions ahead (C = the power of two N/16 rounded down, at
+ * least 8), and the per-position products of all layers share one launch
+ * each. Each layer after the first projects its queries and ephemeral pairs
+ * in chunks of C positions as its input becomes available; a blocked step
+ * whose block reaches queries not yet projected applies it to them when
+ * their chunk is, before any later step, so every query merges the same
+ * blocks in the same order as layer by layer. The naive schedule and the
+ * Transformer layer run layer after layer. Buffers must not overlap.
+ * n_layers: 1..1024.
+ */
+size_t rt_stack_workspace_bytes(const rt_layer_desc* desc, int32_t n_layers);
+rt_status rt_stack_forward(const rt_layer_desc* desc, int32_t n_layers, const rt_layer_weights* w,
+                           const void* x, void* const* z, void* const* k_cache, void* const* v_cache,
+                           void* workspace, size_t workspace_bytes, rt_stream_t stream);
+/* The stack's launches recorded as one HIP graph (launch and destroy it as a
+ * layer plan; the same lifetime rules). */
+rt_status rt_stack_plan_create(const rt_layer_desc* desc, int32_t n_layers, const rt_layer_weights* w,
+                               const void* x, void* const* z, void* const* k_cache, void* const* v_cache,
+                               void* workspace, size_t workspace_bytes, rt_plan** plan);
 
 /*
  * rt_schedule_step -- the integer rule of the blocked schedule on the host

@@ -264,3 +264,33 @@ def test_layer_backward_validates_its_arguments(lib):
     with pytest.raises(rt.RtError) as e:
         rt.rt_layer_backward(d, W, FAKE, FAKE, FAKE, FAKE, G, FAKE + 16, need, stream=0)
     assert "256-byte" in str(e.value)
+
+
+def test_stack_workspace_and_arguments(lib):
+    d = _layer()
+    one = rt.rt_layer_workspace_bytes(d)
+    for n in (1, 2, 6):
+        assert rt.rt_stack_workspace_bytes(d, n) == n * one
+    assert rt.rt_stack_workspace_bytes(d, 0) == 0
+    assert rt.rt_stack_workspace_bytes(d, 1025) == 0
+    assert rt.rt_stack_workspace_bytes(_layer(d_model=100), 2) == 0
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    need = rt.rt_stack_workspace_bytes(d, 2)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_stack_forward(d, [W, W], FAKE, [FAKE, FAKE], [FAKE, FAKE], [FAKE, FAKE], FAKE, need - 1, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(rt.RtError) as e:  # layer 1's weights
+        rt.rt_stack_forward(d, [W, dict(W, w_1=None)], FAKE, [FAKE, FAKE], [FAKE, FAKE], [FAKE, FAKE], FAKE, need,
+                            stream=0)
+    assert e.value.status == 1 and "layer 1" in str(e.value) and "w_1 is NULL" in str(e.value)
+    with pytest.raises(rt.RtError) as e:  # layer 1's input is layer 0's output
+        rt.rt_stack_forward(d, [W, W], FAKE, [FAKE + 8, FAKE], [FAKE, FAKE], [FAKE, FAKE], FAKE, need, stream=0)
+    assert "layer 0" in str(e.value) and "aligned" in str(e.value)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_stack_plan_create(d, [W, W], FAKE, [FAKE, FAKE], [FAKE, None], [FAKE, FAKE], FAKE, need)
+    assert e.value.status == 1 and "k_cache is NULL" in str(e.value)
+    with pytest.raises(ValueError):
+        rt.rt_stack_forward(d, [W, W], FAKE, [FAKE], [FAKE, FAKE], [FAKE, FAKE], FAKE, need, stream=0)
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_stack_forward(d, [], FAKE, [], [], [], FAKE, need, stream=0)
+    assert e.value.status == 1 and "n_layers" in str(e.value)
