@@ -494,6 +494,7 @@ rt_status enqueue_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weigh
     RT_TRY(project(ly[0], N));  // the first layer's input is given: every position up front
 
     std::vector<GemmArgs> go, g1, g2, gk, gku;
+    std::vector<UpdateArgs> steps;
     std::vector<int32_t> act;
     const int64_t ticks = (int64_t)N + (int64_t)(nl - 1) * lag;
     for (int64_t tau = 1; tau <= ticks; ++tau) {
@@ -534,10 +535,27 @@ rt_status enqueue_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weigh
         RT_TRY(run.check(launch_gemm_group(dt, GemmKind::WO, go.data(), (int)go.size(), s), "output projections"));
         RT_TRY(run.check(launch_gemm_group(dt, GemmKind::W1, g1.data(), (int)g1.size(), s), "mlp up"));
         RT_TRY(run.check(launch_gemm_group(dt, GemmKind::W2, g2.data(), (int)g2.size(), s), "mlp down"));
-        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV_UPDATE, gku.data(), (int)gku.size(), s),
-                         "persistent kv projections + small steps"));
-        RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV, gk.data(), (int)gk.size(), s),
-                         "persistent kv projections"));
+        if (gku.size() >= 2) {
+            // several small steps: all the layers' pair projections in one launch
+            // (larger tiles), then the steps in one launch (the fused form runs its
+            // steps on the projection's 32-row tiles: 58.9 us per tick of six
+            // layers, against 24.1 + the steps' own launch)
+            steps.clear();
+            for (GemmArgs& g : gku) {
+                steps.push_back(g.upd);
+                g.upd = UpdateArgs{};
+                gk.push_back(g);
+            }
+            RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV, gk.data(), (int)gk.size(), s),
+                             "persistent kv projections"));
+            RT_TRY(run.check(launch_update_small_group(dt, dh, steps.data(), (int)steps.size(), s),
+                             "small blocked steps"));
+        } else {
+            RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV_UPDATE, gku.data(), (int)gku.size(), s),
+                             "persistent kv projection + small step"));
+            RT_TRY(run.check(launch_gemm_group(dt, GemmKind::KV, gk.data(), (int)gk.size(), s),
+                             "persistent kv projections"));
+        }
         for (int32_t l : act) {
             Stacked& y = ly[l];
             const int32_t t = (int32_t)(tau - (int64_t)l * lag);

@@ -35,6 +35,11 @@ struct UpdateArgs {
 };
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);
+// n blocked steps of 1, 2 or 4 pairs (all the same length, the same pair count;
+// bf16, head_dim 64), kMaxUpdateGroup per launch: the small steps of the layers
+// of a stack.
+constexpr int kMaxUpdateGroup = 8;
+hipError_t launch_update_small_group(rt_dtype dt, int head_dim, const UpdateArgs* us, int n, hipStream_t s);
 // Plain causal attention over nq positions: query row i attends key/value rows
 // 0..i of k/v and is written to row i of a_out ([nq][P][dh]); m/l/o unused.
 hipError_t launch_causal_attention(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);

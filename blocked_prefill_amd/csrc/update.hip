@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
 // finite, and their values are zeroed (their addresses fall back to the
 // query's own, a valid location).
 template <typename T, int DH, int U>
-__global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
+__device__ __forceinline__ void small_step(const UpdateArgs& a) {
     constexpr int G = DH / 8;
     const int64_t pg = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // pair * G + lane
     if (pg >= a.P * G) return;  // whole groups leave together
@@ -202,6 +202,23 @@ __global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
             store8(a.o + sidx * DH + lane * 8, ob);
         }
     }
+}
+
+template <typename T, int DH, int U>
+__global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
+    small_step<T, DH, U>(a);
+}
+
+// The small steps of several sequences' layers in one launch (blockIdx.z picks
+// the step; every step has the same block length U and pair count P, query
+// counts may differ).
+struct UpdateGroup {
+    UpdateArgs a[kMaxUpdateGroup];
+};
+
+template <typename T, int DH, int U>
+__global__ __launch_bounds__(256) void update_small_group_kernel(UpdateGroup g) {
+    small_step<T, DH, U>(g.a[blockIdx.z]);
 }
 
 // Workgroup barrier ordering LDS accesses only: global loads stay in flight across it.
@@ -804,6 +821,38 @@ static hipError_t launch_typed(int head_dim, const UpdateArgs& a, hipStream_t s)
         case 128: return launch_simt<T, 128, CAUSAL>(a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_update_small_group(rt_dtype dt, int head_dim, const UpdateArgs* us, int n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    if (n > kMaxUpdateGroup) {
+        for (int i0 = 0; i0 < n; i0 += kMaxUpdateGroup) {
+            const hipError_t e = launch_update_small_group(dt, head_dim, us + i0,
+                                                           n - i0 < kMaxUpdateGroup ? n - i0 : kMaxUpdateGroup, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    const int U = us[0].nkv;
+    if (dt != RT_BF16 || head_dim != 64 || !(U == 1 || U == 2 || U == 4)) return hipErrorInvalidValue;
+    int64_t max_nq = 0;
+    for (int i = 0; i < n; ++i) {
+        if (us[i].nkv != U || us[i].P != us[0].P || us[i].nq < 0) return hipErrorInvalidValue;
+        max_nq = us[i].nq > max_nq ? us[i].nq : max_nq;
+    }
+    if (max_nq == 0) return hipSuccess;
+    UpdateGroup g{};
+    for (int i = 0; i < n; ++i) g.a[i] = us[i];
+    constexpr int DH = 64;
+    const dim3 grid((uint32_t)((us[0].P * (DH / 8) + 255) / 256), (uint32_t)(max_nq < 65535 ? max_nq : 65535),
+                    (uint32_t)n);
+    if (U == 1)
+        hipLaunchKernelGGL((update_small_group_kernel<bf16, DH, 1>), grid, dim3(256), 0, s, g);
+    else if (U == 2)
+        hipLaunchKernelGGL((update_small_group_kernel<bf16, DH, 2>), grid, dim3(256), 0, s, g);
+    else
+        hipLaunchKernelGGL((update_small_group_kernel<bf16, DH, 4>), grid, dim3(256), 0, s, g);
+    return hipGetLastError();
 }
 
 // Blocks of at least this many pairs go to the MFMA kernel (bf16, head_dim 64).
