@@ -618,9 +618,10 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     // ahead in the tall products with fp32 operands in the epilogue (register
     // budget: 2 waves per SIMD). Several per-position products in one launch
     // (the layers of a stack) fill the chip, and larger tiles then win: for six
-    // products of 512 rows, W_1 128x128 46.8 us against 58.8 with the
-    // per-position tile, W_2 128x128 with 2 K groups 45.2 against 77.4, W_o
-    // 64x64 18.9 against 25.6, W_kv 128x128 25.3 against 38.6.
+    // products of 512 rows, W_1 128x128 (four waves side by side, 128x32 each)
+    // 44.8 us against 58.8 with the per-position tile (48.3 with 2x2 waves),
+    // W_2 128x128 with 2 K groups 44.3 against 77.4, W_o 64x64 18.9 against
+    // 25.6, W_kv 128x128 25.3 against 38.6.
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1) {
@@ -649,16 +650,18 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
         case GemmKind::W1:
-            if constexpr (KS == 1)
-                return big || grouped ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
-                                      : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(gs, s);
+            if constexpr (KS == 1) {
+                if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 1, 4, 2, 32>(gs, s);
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
+                           : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(gs, s);
+            }
             break;
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
             if constexpr (KS == 1) {
                 if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
             }
             if constexpr (KS == 2) {
-                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, D, 32, 2>(gs, s);
+                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32, 2>(gs, s);
             }
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
