@@ -104,10 +104,11 @@ def _run_stack(desc, x, ws, dt):
     return st
 
 
-@pytest.mark.parametrize("n", [300, 37])
+@pytest.mark.parametrize("n", [300, 37, 2, 1])
 def test_stack_f32_equals_layer_by_layer(n):
     """N=300: chunks of 16 positions, so steps of 32..256 pairs defer rows; N=37:
-    chunks of 8, the step of 16 pairs defers rows 25..32."""
+    chunks of 8, the step of 16 pairs defers rows 25..32; N=1 and 2: each layer's
+    whole sequence inside the lag."""
     import torch
     dt, b, d, h, f, L = "f32", 2, 96, 3, 128, 3
     x, ws, scale, desc = _case(dt, n, b, d, h, f, L, seed=10 + n)
@@ -121,9 +122,9 @@ def test_stack_f32_equals_layer_by_layer(n):
         xin = one.z
 
 
-@pytest.mark.parametrize("n,qk,rho,gains", [(100, False, 1.0, True), (100, False, 1.0 / math.sqrt(6.0), True),
-                                           (100, True, 1.0, False)])
-def test_stack_bf16_each_layer_matches_oracle(n, qk, rho, gains):
+@pytest.mark.parametrize("n,qk,rho,gains,h", [(100, False, 1.0, True, 4), (100, False, 1.0 / math.sqrt(6.0), True, 4),
+                                             (100, True, 1.0, False, 4), (100, False, 1.0, True, 8)])
+def test_stack_bf16_each_layer_matches_oracle(n, qk, rho, gains, h):
     """Each layer on its actual input (the stack's previous output): against the
     oracle (the parity bars) and against the single-layer path. N=100 has chunks
     of 8 positions: steps of 16..64 pairs defer rows. (The bf16 recurrence
@@ -134,7 +135,7 @@ def test_stack_bf16_each_layer_matches_oracle(n, qk, rho, gains):
     weights, rounded to bf16, and the per-head norm amplifies that rounding
     where a head's vector is small; with both, the single-layer path itself
     reaches 0.028 beyond the half-ulp on this case, the stack equal to it.)"""
-    dt, b, d, h, f, L = "bf16", 3, 256, 4, 512, 3
+    dt, b, d, f, L = "bf16", 3, 256, 512, 3  # h = 8: head_dim 32, whose small steps run per layer
     flags = rt.RT_FLAG_QK_NORM if qk else 0
     x, ws, scale, desc = _case(dt, n, b, d, h, f, L, seed=20 + n, qk=qk, flags=flags, rho=rho, gains=gains)
     st = _run_stack(desc, x, ws, dt)
