@@ -409,9 +409,9 @@ int32_t stack_chunk(int32_t n) {
 // 1, 2 and 4 pairs at the same ticks in every layer).
 //
 // The blocked schedule is kept exactly. Step t applies its block to queries
-// t+1..t+b; those not yet projected (only when b >= C, t = kC: rows past
-// t + C) are applied when their chunk is projected, before any later step
-// touches them. Every query thus merges the same blocks in the same order as
+// t+1..t+b; those not yet projected (only when b > C, at t = kC: rows past
+// t + C) get it when their chunk is projected, before any later step touches
+// them (a step t' < (k+1)C reaches rows up to t' + lowbit(t') <= (k+1)C). Every query thus merges the same blocks in the same order as
 // in the layer-by-layer run; a block of b > C pairs is read once per chunk of
 // its deferred rows instead of once.
 rt_status enqueue_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weights* w, const void* x,
