@@ -178,6 +178,90 @@ def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_t
     return np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)])  # ms
 
 
+def update_only_bench(args, rt, wl):
+    """The isolated blocked update (no layer around it): one step = the whole
+    sequence's blocked attention with every pair known up front (rt_attn_forward:
+    position 1, then each level of the schedule in one launch), replayed as one
+    HIP graph on seeded q, k', v', k, v resident in HBM. value = B*N / step
+    time; roofline = the steps' algorithmic bytes over the step time."""
+    import numpy as np
+    import torch
+    import oracle
+    import rt_inputs
+    N, B, H, dh = wl.n_pos, wl.batch, wl.n_heads, wl.head_dim
+    D, P = H * dh, B * H
+    scale = 1.0 / math.sqrt(dh)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    t_np = rt_inputs.attn_inputs(wl)
+    bf = {k: torch.from_numpy(v.reshape(N, B, D)).to(torch.bfloat16).to(dev) for k, v in t_np.items()}
+    del t_np
+    m = torch.empty((N, B, H), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    o = torch.empty((N, B, D), dtype=torch.float32, device=dev)
+    a = torch.empty((N, B, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((N, B, H), dtype=torch.float32, device=dev)
+    desc = rt.AttnDesc(batch=B, seq_len=N, n_heads=H, head_dim=dh, dtype=rt.RT_BF16, softmax_scale=scale)
+    levels = 1 + max(0, (N - 1).bit_length())  # position 1's finalize + one launch per block size
+
+    def sequence(st):
+        rt.rt_attn_forward(desc, bf["q"], bf["k_eph"], bf["v_eph"], bf["k"], bf["v"], a, lse, m, l, o, st)
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            sequence(cap)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup} done")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = B * N / (ms / 1e3)
+    assert bool(torch.isfinite(a).all()), "non-finite output"
+    byts = np.array([update_bytes(t, N, P, dh, 2) for t in range(1, N)], dtype=np.float64)
+    flops = np.array([update_flops(t, N, P, dh) for t in range(1, N)], dtype=np.float64)
+    avg_s = ms / 1e3 / levels
+    achieved = byts.sum() / (ms / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
+        f"{achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
+    cpu = None
+    if not args.no_cpu:
+        rows = list(range(min(args.cpu_rows, B)))
+        tr = rt_inputs.attn_inputs(wl, rows=rows)
+        t0 = time.time()
+        oracle.attention(tr["q"], tr["k_eph"], tr["v_eph"], tr["k"], tr["v"], scale)
+        cpu_s = time.time() - t0
+        cpu = {"value": round(len(rows) * N / cpu_s, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"{len(rows)} batch rows x all {N} positions ({cpu_s:.1f} s)"}
+        log(f"cpu oracle: {cpu_s:.1f}s for the sample")
+    out = {
+        "metric": "blocked-update tokens/s (isolated update, HBM GB/s)", "value": round(tokens_per_s, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k', v', k, v)",
+        "config": {"workload": f"{wl.name}: isolated blocked update, bf16 inputs, fp32 state, B={B}, "
+                               f"{H} heads x {dh}, N={N}", "batch": B, "seq_len": N},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "fused blocked update + finalize, one launch per level", "launches": levels,
+                     "avg_launch_us": round(avg_s * 1e6, 2), "alg_bytes_per_launch": int(byts.sum() / levels)},
+        "mfma_util": {"scope": "the update's scores and values (4*dh flops per visited (query, key) pair)",
+                      "achieved_TFLOP_s": round(flops.sum() / (ms / 1e3) / 1e12, 1), "peak_TFLOP_s": 2500.0,
+                      "frac": round(flops.sum() / (ms / 1e3) / 1e12 / 2500.0, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 SWEEP_VARIANTS = {"rt_blocked": 0, "rt_naive": 2, "transformer": 4}  # rt_layer_desc flags
 
 
@@ -418,6 +502,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-positions", type=int, default=0,
+                    help="CPU sample: the first P positions only (default: all, or 2048 when N > 8192; "
+                         "outputs at positions <= P depend on those positions only)")
     ap.add_argument("--counters", action="store_true",
                     help="short run for hardware-counter passes: one layer forward, then its update "
                          "sequence, then a plain 1 GiB device copy (the calibration kernel)")
@@ -463,6 +550,8 @@ def main():
     if args.layer_backward:
         return layer_backward_bench(args)
     wl = rt_inputs.WORKLOADS[args.workload]
+    if wl.update_only:
+        return update_only_bench(args, rt, wl)
     N, B, D, H, dh, F, L = wl.n_pos, wl.batch, wl.d_model, wl.n_heads, wl.head_dim, wl.d_ff, wl.n_layers
     scale = 1.0 / math.sqrt(dh)
     dev = torch.device("cuda", 0)
@@ -605,17 +694,20 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        rows = list(range(args.cpu_rows))
-        xr = rt_inputs.layer_input(wl, rows=rows)
+        rows = list(range(min(args.cpu_rows, B)))
+        # long sequences: a prefix keeps the naive oracle (quadratic in N) within seconds
+        npos = args.cpu_positions if 0 < args.cpu_positions < N else (2048 if N > 8192 else N)
+        xr = rt_inputs.layer_input(wl, rows=rows)[:npos]
         w0 = rt_inputs.layer_weights(wl, 0)
         t0 = time.time()
         oracle.layer_forward(xr, w0, n_heads=H, softmax_scale=scale, round_bf16=True)
         cpu_s = time.time() - t0
         # the sample is one of the stack's L layers: the stack rate is L times slower
-        cpu_value = len(rows) * N / (cpu_s * L)
+        cpu_value = len(rows) * npos / (cpu_s * L)
+        span = f"all {N} positions" if npos == N else f"the first {npos} of {N} positions (later ones cost more)"
         cpu = {"value": round(cpu_value, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{len(rows)} batch rows x all {N} positions x layer 1 of {L} "
-                         f"({cpu_s:.1f} s); stack rate = rows*N/({L}*time)"}
+               "sample": f"{len(rows)} batch rows x {span} x layer 1 of {L} "
+                         f"({cpu_s:.1f} s); stack rate = rows*positions/({L}*time)"}
         log(f"cpu oracle: {cpu_s:.1f}s for the sample -> {cpu_value:.1f} stack tokens/s")
 
     out = {

@@ -141,6 +141,28 @@ Layout layout_of(const rt_layer_desc* d, Mode mode) {
     return L;
 }
 
+// A capture in progress on this thread (plans): the launches are recorded
+// into graphs of at most `limit` launches each, ended and begun again on the
+// capture stream (one graph with ~10^5 nodes of a long sequence did not
+// survive instantiation; a chain of graphs replays the same launches in order).
+struct CaptureSegments {
+    hipStream_t s;
+    int limit = 8192;
+    int count = 0;
+    std::vector<hipGraph_t> graphs;
+    rt_status cut() {
+        hipGraph_t g = nullptr;
+        hipError_t e = hipStreamEndCapture(s, &g);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamEndCapture");
+        graphs.push_back(g);
+        e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamBeginCapture");
+        count = 0;
+        return RT_OK;
+    }
+};
+thread_local CaptureSegments* g_capture = nullptr;
+
 struct Launcher {
     hipStream_t s;
     bool debug;
@@ -150,6 +172,7 @@ struct Launcher {
             e = hipStreamSynchronize(s);
             if (e != hipSuccess) return hip_fail(e, what);
         }
+        if (g_capture && g_capture->s == s && ++g_capture->count >= g_capture->limit) return g_capture->cut();
         return RT_OK;
     }
 };
@@ -603,6 +626,35 @@ rt_status enqueue_decode(const rt_layer_desc* d, const rt_layer_weights* w, int3
 
 // ---------------------------------------------------------------- backward
 
+// The blocked attention of a whole sequence whose pairs are all known up front
+// (u: q, k, v, k', v', m, l, o, lse, P and sigma2 set; a: [N][B][H][dh]
+// outputs, slab bytes per position): position 1, then the schedule's levels
+// from the largest block down, each level's steps in one launch. A query's
+// blocks shrink from step to step, so it merges them in step order; each
+// step's first query is finished by its level's launch, after its larger
+// blocks.
+rt_status enqueue_attention_levels(rt_dtype dt, int32_t dh, rt::UpdateArgs u, int32_t N, char* a, size_t slab,
+                                   Launcher& run) {
+    using namespace rt;
+    u.a_out = a; u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1; u.n_steps = 1;
+    RT_TRY(run.check(launch_update(dt, dh, u, run.s), "finalize position 1"));
+    int32_t top = 1;  // the largest power of two below N
+    while ((int64_t)top * 2 < N) top *= 2;
+    for (int32_t b = top; b >= 1 && b < N; b /= 2) {
+        const int32_t steps = (N - 1 - b) / (2 * b) + 1;  // t = b, 3b, 5b, ... < N
+        for (int32_t s0 = 0; s0 < steps; s0 += 65535) {
+            const int32_t ns = steps - s0 < 65535 ? steps - s0 : 65535;
+            const int32_t t = b + 2 * b * s0;  // this launch's first step
+            u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
+            u.init = (t == b); u.fin = 1;
+            u.a_out = a + (size_t)t * slab; u.a_step = (int64_t)(2 * (size_t)b * slab);
+            u.n_steps = ns; u.n_pos = N;
+            RT_TRY(run.check(launch_update(dt, dh, u, run.s), "blocked attention level"));
+        }
+    }
+    return RT_OK;
+}
+
 rt_status check_backward(const rt_layer_desc* d) {
     RT_TRY(check_layer(d));
     if (d->flags & RT_FLAG_TRANSFORMER) return fail(RT_ERR_UNSUPPORTED, "the backward covers the RT layer only");
@@ -715,16 +767,7 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
         u.q = at(L.q); u.k = at(L.kc); u.v = at(L.vc); u.k_eph = at(L.ke); u.v_eph = at(L.ve);
         u.m = f32(L.m); u.l = f32(L.l); u.o = f32(L.o); u.lse = f32(L.lse); u.P = P;
         u.sigma2 = d->attn.softmax_scale * kLog2eHost;
-        const size_t slab = (size_t)B * D * es;
-        u.a_out = at(L.a); u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
-        RT_TRY(run.check(launch_update(dt, dh, u, s), "attention recompute"));
-        for (int32_t t = 1; t < N; ++t) {
-            const int32_t b = block_of(t);
-            u.a_out = base + L.a + (size_t)t * slab;
-            u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
-            u.init = (b == t); u.fin = 1;
-            RT_TRY(run.check(launch_update(dt, dh, u, s), "attention recompute"));
-        }
+        RT_TRY(enqueue_attention_levels(dt, dh, u, N, base + L.a, (size_t)B * D * es, run));
     }
     {   // h = x + rho W_o a (and, in bf16 layers, its bf16 copy and partial sums of h^2)
         GemmArgs go{};
@@ -843,8 +886,8 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
 }  // namespace
 
 struct rt_plan {
-    hipGraph_t graph = nullptr;
-    hipGraphExec_t exec = nullptr;
+    std::vector<hipGraph_t> graphs;    // replayed in order
+    std::vector<hipGraphExec_t> execs;
 };
 
 namespace {
@@ -866,34 +909,47 @@ rt_status check_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weights
     return RT_OK;
 }
 
-// Capture what enqueue puts on a stream into a HIP graph, instantiated.
+// Capture what enqueue puts on a stream into HIP graphs (see CaptureSegments), instantiated.
 template <typename F>
 rt_status capture_plan(F&& enqueue, rt_plan** plan) {
     hipStream_t cs;
     hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
     if (e != hipSuccess) return hip_fail(e, "capture stream");
     rt_plan* p = new rt_plan();
+    auto drop = [&](rt_status st) {
+        for (hipGraphExec_t x : p->execs) (void)hipGraphExecDestroy(x);
+        for (hipGraph_t g : p->graphs) (void)hipGraphDestroy(g);
+        delete p;
+        return st;
+    };
     e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
     if (e != hipSuccess) {
         (void)hipStreamDestroy(cs);
-        delete p;
-        return hip_fail(e, "hipStreamBeginCapture");
+        return drop(hip_fail(e, "hipStreamBeginCapture"));
     }
+    CaptureSegments seg;
+    seg.s = cs;
+    g_capture = &seg;
     rt_status st = enqueue(cs);
-    hipGraph_t graph = nullptr;
-    e = hipStreamEndCapture(cs, &graph);
+    g_capture = nullptr;
+    hipGraph_t last = nullptr;
+    e = hipStreamEndCapture(cs, &last);
     (void)hipStreamDestroy(cs);
-    if (st != RT_OK || e != hipSuccess) {
-        if (graph) (void)hipGraphDestroy(graph);
-        delete p;
-        return st != RT_OK ? st : hip_fail(e, "hipStreamEndCapture");
+    p->graphs = std::move(seg.graphs);
+    if (last) {
+        size_t nodes = 0;  // a capture cut right after the last launch leaves an empty graph
+        if (hipGraphGetNodes(last, nullptr, &nodes) == hipSuccess && nodes == 0 && !p->graphs.empty())
+            (void)hipGraphDestroy(last);
+        else
+            p->graphs.push_back(last);
     }
-    p->graph = graph;
-    e = hipGraphInstantiate(&p->exec, graph, nullptr, nullptr, 0);
-    if (e != hipSuccess) {
-        (void)hipGraphDestroy(graph);
-        delete p;
-        return hip_fail(e, "hipGraphInstantiate");
+    if (st != RT_OK) return drop(st);
+    if (e != hipSuccess) return drop(hip_fail(e, "hipStreamEndCapture"));
+    for (hipGraph_t g : p->graphs) {
+        hipGraphExec_t x = nullptr;
+        e = hipGraphInstantiate(&x, g, nullptr, nullptr, 0);
+        if (e != hipSuccess) return drop(hip_fail(e, "hipGraphInstantiate"));
+        p->execs.push_back(x);
     }
     *plan = p;
     return RT_OK;
@@ -1007,22 +1063,12 @@ rt_status rt_attn_forward(const rt_attn_desc* desc, const void* q, const void* k
         return fail(RT_ERR_INVALID_ARG, "lse, m and l must be 4-byte aligned");
     const int32_t N = desc->seq_len;
     const size_t slab = (size_t)desc->batch * desc->n_heads * desc->head_dim * elem_bytes(desc->dtype);
-    hipStream_t s = (hipStream_t)stream;
     rt::UpdateArgs u{};
     u.q = q; u.k = k; u.v = v; u.k_eph = k_eph; u.v_eph = v_eph; u.m = m; u.l = l; u.o = o; u.lse = lse;
     u.P = (int64_t)desc->batch * desc->n_heads;
     u.sigma2 = desc->softmax_scale * rt::kLog2eHost;
-    // position 1, then the fused steps t = 1..N-1 (each finishing position t+1)
-    u.a_out = a; u.kv0 = 0; u.nkv = 0; u.q0 = 0; u.nq = 1; u.init = 1; u.fin = 1;
-    hipError_t e = rt::launch_update(desc->dtype, desc->head_dim, u, s);
-    for (int32_t t = 1; t < N && e == hipSuccess; ++t) {
-        const int32_t b = block_of(t);
-        u.a_out = (char*)a + (size_t)t * slab;
-        u.kv0 = t - b; u.nkv = b; u.q0 = t; u.nq = (b < N - t) ? b : N - t;
-        u.init = (b == t); u.fin = 1;
-        e = rt::launch_update(desc->dtype, desc->head_dim, u, s);
-    }
-    return e == hipSuccess ? RT_OK : hip_fail(e, "rt_attn_forward launch");
+    Launcher run{(hipStream_t)stream, false};
+    return enqueue_attention_levels(desc->dtype, desc->head_dim, u, N, (char*)a, slab, run);
 }
 
 rt_status rt_attn_backward(const rt_attn_desc* desc, const void* q, const void* k_eph, const void* v_eph,
@@ -1174,15 +1220,18 @@ rt_status rt_stack_plan_create(const rt_layer_desc* desc, int32_t n_layers, cons
 }
 
 rt_status rt_layer_plan_launch(rt_plan* plan, rt_stream_t stream) {
-    if (!plan || !plan->exec) return fail(RT_ERR_INVALID_ARG, "plan is NULL");
-    hipError_t e = hipGraphLaunch(plan->exec, (hipStream_t)stream);
-    return e == hipSuccess ? RT_OK : hip_fail(e, "hipGraphLaunch");
+    if (!plan || plan->execs.empty()) return fail(RT_ERR_INVALID_ARG, "plan is NULL");
+    for (hipGraphExec_t x : plan->execs) {
+        hipError_t e = hipGraphLaunch(x, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+    }
+    return RT_OK;
 }
 
 void rt_layer_plan_destroy(rt_plan* plan) {
     if (!plan) return;
-    if (plan->exec) (void)hipGraphExecDestroy(plan->exec);
-    if (plan->graph) (void)hipGraphDestroy(plan->graph);
+    for (hipGraphExec_t x : plan->execs) (void)hipGraphExecDestroy(x);
+    for (hipGraph_t g : plan->graphs) (void)hipGraphDestroy(g);
     delete plan;
 }
 

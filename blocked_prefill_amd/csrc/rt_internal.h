@@ -32,6 +32,13 @@ struct UpdateArgs {
     int32_t init;       // state rows are initialised, not read (first touch)
     int32_t fin;        // row q0 is finished into a_out and its state is not written
     float* lse;         // [N][P] (nullable): base-2 log-sum-exp of the finished row, m + log2(l)
+    // Several steps of one level in one launch (every pair known up front):
+    // n_steps steps, step s applying keys kv0 + 2s*nkv.. to queries q0 + 2s*nkv..
+    // (query count clipped at n_pos; only step 0 initialises its rows; step s
+    // finishes into a_out + s*a_step bytes). 0 or 1: one step.
+    int32_t n_steps;
+    int32_t n_pos;
+    int64_t a_step;
 };
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s);

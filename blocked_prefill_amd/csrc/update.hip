@@ -13,6 +13,21 @@
 
 namespace rt {
 
+// Step s of a launch that runs several steps of one level (UpdateArgs::n_steps).
+// The steps of one level touch distinct query rows: step t's rows t+1..t+b lie
+// between consecutive odd multiples of b.
+__device__ __forceinline__ UpdateArgs level_step(const UpdateArgs& in, int s) {
+    UpdateArgs a = in;
+    if (s > 0) {
+        const int32_t shift = s * 2 * in.nkv;
+        a.kv0 += shift;
+        a.q0 += shift;
+        a.nq = min(in.nkv, in.n_pos - a.q0);
+        a.init = 0;
+        a.a_out = (char*)in.a_out + (int64_t)s * in.a_step;
+    }
+    return a;
+}
 
 // SIMT update: one item = (query row i, batch*head pair p), handled by a
 // group of DH/8 consecutive lanes, each holding 8 of the DH components.
@@ -20,7 +35,8 @@ namespace rt {
 // 16-byte pieces of the position-major q / k / v / state slabs.
 // CAUSAL: plain causal attention, as in the MFMA kernel below.
 template <typename T, int DH, bool CAUSAL>
-__global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a) {
+__global__ __launch_bounds__(256) void update_simt_kernel(UpdateArgs a_in) {
+    const UpdateArgs a = level_step(a_in, blockIdx.y);
     constexpr int G = DH / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t item = gid / G;
@@ -206,7 +222,7 @@ __device__ __forceinline__ void small_step(const UpdateArgs& a) {
 
 template <typename T, int DH, int U>
 __global__ __launch_bounds__(256) void update_small_kernel(UpdateArgs a) {
-    small_step<T, DH, U>(a);
+    small_step<T, DH, U>(level_step(a, blockIdx.z));
 }
 
 // The small steps of several sequences' layers in one launch (blockIdx.z picks
@@ -255,7 +271,9 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // queries' own positions (kv0 = q0 = 0); query i takes key rows 0..i and is
 // written to row i of a_out; no state is read or written.
 template <int WAVES, int KT, bool RAGGED, bool CAUSAL>
-__global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, int nqt) {
+__global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in, int nqt) {
+    const UpdateArgs a = level_step(a_in, blockIdx.y);
+    if (a.nq <= 0) return;  // the whole workgroup
     constexpr int DH = 64;
     constexpr int KSTR = DH + 8;    // bf16 per K row in LDS (16-byte pad)
     constexpr int VSTR = KT + 8;    // bf16 per V^T row in LDS
@@ -562,7 +580,8 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a, i
 // two lanes. One key/value tile, no running maximum; the stored state is
 // fetched together with the tile.
 template <int PPW>
-__global__ __launch_bounds__(64) void update_mfma_multi_kernel(UpdateArgs a) {
+__global__ __launch_bounds__(64) void update_mfma_multi_kernel(UpdateArgs a_in) {
+    const UpdateArgs a = level_step(a_in, blockIdx.y);
     constexpr int DH = 64, KB = 32 / PPW;  // keys (and at most as many queries) per pair
     constexpr int KSTR = DH + 8, VSTR = 32 + 8;
     static_assert(PPW == 2 || PPW == 4, "pairs per wave");
@@ -773,7 +792,7 @@ __global__ __launch_bounds__(64) void update_mfma_multi_kernel(UpdateArgs a) {
 template <int WAVES, bool CAUSAL = false>
 static hipError_t launch_mfma(const UpdateArgs& a, hipStream_t s) {
     const int nqt = (a.nq + 32 * WAVES - 1) / (32 * WAVES);
-    const dim3 grid((uint32_t)(a.P * nqt)), block(64 * WAVES);
+    const dim3 grid((uint32_t)(a.P * nqt), (uint32_t)(a.n_steps > 1 ? a.n_steps : 1)), block(64 * WAVES);
     // the plain instances address a tile's rows with 32-bit byte offsets
     const bool offsets_fit = (uint64_t)a.P * 64 * 2 * 64 <= 0xffffffffull;
     if constexpr (CAUSAL) {
@@ -797,7 +816,8 @@ static hipError_t launch_simt(const UpdateArgs& a, hipStream_t s) {
     if constexpr (!CAUSAL && sizeof(T) == 2) {
         // blocks of 1, 2 and 4 pairs (most steps of the blocked schedule): one round trip
         if (a.nkv == 1 || a.nkv == 2 || a.nkv == 4) {
-            const dim3 grid((uint32_t)((a.P * (DH / 8) + 255) / 256), (uint32_t)(a.nq < 65535 ? a.nq : 65535));
+            const dim3 grid((uint32_t)((a.P * (DH / 8) + 255) / 256), (uint32_t)(a.nq < 65535 ? a.nq : 65535),
+                            (uint32_t)(a.n_steps > 1 ? a.n_steps : 1));
             if (a.nkv == 1)
                 hipLaunchKernelGGL((update_small_kernel<T, DH, 1>), grid, dim3(256), 0, s, a);
             else if (a.nkv == 2)
@@ -809,7 +829,8 @@ static hipError_t launch_simt(const UpdateArgs& a, hipStream_t s) {
     }
     const int64_t threads = (int64_t)a.nq * a.P * (DH / 8);
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL((update_simt_kernel<T, DH, CAUSAL>), dim3((uint32_t)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((update_simt_kernel<T, DH, CAUSAL>), dim3((uint32_t)blocks, (uint32_t)(a.n_steps > 1 ? a.n_steps : 1)),
+                       dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -860,10 +881,12 @@ constexpr int kMfmaMinBlock = 32;
 
 hipError_t launch_update(rt_dtype dt, int head_dim, const UpdateArgs& a, hipStream_t s) {
     if (a.nq <= 0) return hipSuccess;
+    if (a.n_steps > 65535) return hipErrorInvalidConfiguration;  // grid y/z limit
     if (dt == RT_BF16 && head_dim == 64 && a.nkv == 16 && a.nq <= 16 && a.P % 2 == 0) {
         // blocks of 16: two pairs per MFMA wave (blocks of 8, four pairs per wave,
         // measured 14.2 us per step at 8192 pairs against the SIMT kernel's 13.6)
-        hipLaunchKernelGGL((update_mfma_multi_kernel<2>), dim3((uint32_t)(a.P / 2)), dim3(64), 0, s, a);
+        hipLaunchKernelGGL((update_mfma_multi_kernel<2>), dim3((uint32_t)(a.P / 2), (uint32_t)(a.n_steps > 1 ? a.n_steps : 1)),
+                           dim3(64), 0, s, a);
         return hipGetLastError();
     }
     if (dt == RT_BF16 && head_dim == 64 && a.nkv >= kMfmaMinBlock) {

@@ -89,6 +89,32 @@ def test_forward_saves_the_log_sum_exp():
 
 
 @pytest.mark.parametrize("dt,n,b,h,dh", [
+    ("bf16", 300, 3, 8, 64), ("bf16", 1000, 1, 1, 64), ("bf16", 70, 2, 4, 32), ("f32", 77, 2, 3, 32),
+    ("bf16", 3, 2, 2, 64), ("bf16", 2, 2, 2, 64), ("bf16", 1, 2, 2, 64),
+])
+def test_forward_by_levels_equals_the_step_sequence(dt, n, b, h, dh):
+    """rt_attn_forward runs each level of the schedule in one launch (largest
+    blocks first); its outputs equal the steps t = 1..N-1 run one launch each
+    (rt_update_finalize_step, as a layer runs them) bit for bit: every query
+    merges the same blocks in the same order. P = 24 takes the two-pairs-per-wave
+    kernel at 16 pairs, P = 1 the SIMT kernel there."""
+    import torch
+    t = _case(41 + n, n, b, h, dh, dt)
+    scale = 1.0 / math.sqrt(dh)
+    a_levels, _, _ = _run(t, dt, scale)
+    desc = G.attn_desc(b, n, h, dh, dt, scale)
+    q, ke, ve, k, v = (G.dev(t[x], dt) for x in ("q", "k_eph", "v_eph", "k", "v"))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    m, l, o = torch.empty((n, b, h), **f32), torch.empty((n, b, h), **f32), torch.empty((n, b, h, dh), **f32)
+    a_steps = torch.full_like(q, float("nan"))
+    rt.rt_finalize_step(desc, 1, q, ke, ve, m, l, o, a_steps[0])
+    for s_ in range(1, n):  # step s_ fused with the finish of position s_+1, one launch each
+        rt.rt_update_finalize_step(desc, s_, q, ke, ve, k, v, m, l, o, a_steps[s_])
+    torch.cuda.synchronize()
+    assert torch.equal(a_levels, a_steps)
+
+
+@pytest.mark.parametrize("dt,n,b,h,dh", [
     ("f32", 77, 2, 3, 32), ("f32", 1, 2, 2, 64), ("f32", 65, 1, 2, 128),
     ("bf16", 300, 3, 8, 64), ("bf16", 129, 2, 4, 128), ("bf16", 200, 3, 2, 32),
 ])

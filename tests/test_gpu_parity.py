@@ -179,6 +179,29 @@ def test_layer_plan_replays_match_eager(n):
     plan.destroy()
 
 
+def test_layer_plan_of_a_long_sequence_matches_eager():
+    """N = 4096 positions: the plan's ~19k launches are captured as a chain of
+    graphs (at most 8192 launches each); replays equal the eager call bitwise."""
+    import torch
+    n, b, d, h, f = 4096, 2, 256, 4, 512
+    rng = np.random.default_rng(11)
+    x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), "bf16")
+    w = _small_weights(12, d, f, "bf16", gains=False)
+    desc = G.layer_desc(b, n, d, h, f, "bf16", 0.125)
+    buf = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16")
+    buf.forward()
+    torch.cuda.synchronize()
+    z0 = buf.z.clone()
+    plan = buf.plan()
+    for _ in range(2):
+        buf.z.fill_(float("nan"))
+        torch.cuda.synchronize()
+        plan.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.z, z0)
+    plan.destroy()
+
+
 def _run_layer(desc, x_dev, w, dt, use_plan):
     import torch
     buf = G.LayerBuffers(desc, x_dev, w, dt)
