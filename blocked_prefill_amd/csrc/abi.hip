@@ -381,7 +381,9 @@ rt_status enqueue_layer(const rt_layer_desc* d, const rt_layer_weights* w, const
 
     const size_t slab = (size_t)B * d->d_model * es;
     // the blocked schedule's steps of 1, 2 and 4 pairs run inside the K/V projection (bf16, head_dim 64)
-    const bool fuse_small = mode == Mode::Blocked && dt == RT_BF16 && dh == 64;
+    // (not with at most 16 batch rows: the K/V product then runs on 16-row tiles, and the
+    // fused form's one-head-per-tile layout would leave it a few workgroups)
+    const bool fuse_small = mode == Mode::Blocked && dt == RT_BF16 && dh == 64 && B > 16;
     for (int32_t t = 1; t <= N; ++t) {
         const size_t at = (size_t)(t - 1) * slab;
         const int32_t bt = block_of(t);
@@ -454,7 +456,7 @@ rt_status enqueue_stack(const rt_layer_desc* d, int32_t nl, const rt_layer_weigh
     const Layout L = layout_of(d, mode);
     const size_t slab = (size_t)B * d->d_model * es;
     const int32_t C = stack_chunk(N), lag = C + 8;
-    const bool fuse_small = dt == RT_BF16 && dh == 64;
+    const bool fuse_small = dt == RT_BF16 && dh == 64 && B > 16;  // as in enqueue_layer
 
     struct Deferred {
         int32_t kv0, nkv, init;  // the block: key rows kv0..kv0+nkv-1 (0-based); its step initialises the rows

@@ -610,6 +610,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     const GemmArgs& g = gs.g[0];  // the shape and flags every product of the set shares
     const bool big = gs.max_m >= 4096;
     const bool grouped = !big && gs.n >= 2;
+    // at most 16 rows (a small batch, a decode step): 16-row tiles, 32 columns
+    // wide, K split over 2 or 4 wave groups (M = 8: W_o 4.3 us against 5.9 with
+    // the 64-row tiles, W_1 4.6 against 7.6, W_2 8.2 against 12.2, W_kv 4.3
+    // against 6.4; with many more, narrower workgroups streaming the weights)
+    const bool skinny = gs.max_m <= 16 && gs.n == 1;
     // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
     // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave),
     // with K split over 2 or 4 wave groups where that measured faster (W_2,
@@ -642,6 +647,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             break;
         case GemmKind::WO:  // h (fp32) and its bf16 copy, plus partial sums of h^2 for the MLP's RMS
+            if constexpr (KS <= 4) {
+                if (skinny) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 16, 32, 1, 1, D, 16, KS>(gs, s);
+            }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
                 if (grouped) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, D, 16>(gs, s);
@@ -650,6 +658,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
         case GemmKind::W1:
+            if constexpr (KS <= 4) {
+                if (skinny) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 16, 32, 1, 1, D, 16, KS>(gs, s);
+            }
             if constexpr (KS == 1) {
                 if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 1, 4, 2, 32>(gs, s);
                 return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
@@ -657,6 +668,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             break;
         case GemmKind::W2:  // z, plus partial sums of z^2 (as stored) for the persistent pair's RMS
+            if constexpr (KS <= 4) {
+                if (skinny) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 16, 32, 1, 1, D, 16, KS>(gs, s);
+            }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
             }
@@ -674,6 +688,12 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             break;
         case GemmKind::KV:
+            if constexpr (KS <= 4) {
+                if (skinny) {  // the query/key norm needs a head's columns in one tile
+                    if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 16, 64, 1, 2, D, 16, KS>(gs, s);
+                    return run_pipe<bf16, float, EPI_RMS_PARTS, 16, 32, 1, 1, D, 16, KS>(gs, s);
+                }
+            }
             if constexpr (KS == 1) {
                 if (grouped) {
                     if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s);
@@ -711,6 +731,9 @@ static int k_groups(GemmKind kind, const GemmArgs& g, int64_t max_m, int n) {
              : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2
              : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : kind == GemmKind::W2_BWD ? 2 : 1;
     if (n >= 2 && kind != GemmKind::KV_UPDATE) ks = kind == GemmKind::W2 ? 2 : 1;  // several products per launch
+    if (n == 1 && max_m <= 16 && (kind == GemmKind::WO || kind == GemmKind::W1 || kind == GemmKind::W2 ||
+                                  kind == GemmKind::KV))
+        ks = kind == GemmKind::W2 ? 4 : 2;  // at most 16 rows
     const int kt = g.K / 64;
     while (ks > 1 && !(kt % ks == 0 && (kt / ks) % 2 == 0)) ks /= 2;
     return ks;
