@@ -321,9 +321,9 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
     }
 
     constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
-    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes);
+    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes, 256 rows four);
     // each K group stages its partial tile in its own buffers
-    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : BM / 2;
+    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : (BM / 2 * LDT * 4 <= 2 * STAGE) ? BM / 2 : BM / 4;
     static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
     constexpr int CPRW = BN / 8;               // 8-column runs per row
     constexpr int RUNS = (PR * CPRW + NT - 1) / NT;  // runs per thread per pass
@@ -626,7 +626,10 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     // products of 512 rows, W_1 128x128 (four waves side by side, 128x32 each)
     // 44.8 us against 58.8 with the per-position tile (48.3 with 2x2 waves),
     // W_2 128x128 with 2 K groups 44.3 against 77.4, W_o 64x64 18.9 against
-    // 25.6, W_kv 128x128 25.3 against 38.6.
+    // 25.6, W_kv 128x128 25.3 against 38.6. Then W_kv 128x256 with eight waves
+    // 22.9 / 25.6 against 24.9 / 28.0 for 128x128 (two boxes), and W_o's 64x64
+    // prefetching 2 K tiles 18.2 against 19.3 with 4; 256-row or 256-column
+    // tiles measured slower for W_1 (50.5-58.2) and W_2 (60.0-63.1).
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1) {
@@ -652,7 +655,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
-                if (grouped) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, D, 16>(gs, s);
+                if (grouped) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, 2, 16>(gs, s);
             }
             if constexpr (KS <= 2)
                 if (!big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
@@ -697,6 +700,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             if constexpr (KS == 1) {
                 if (grouped) {
                     if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s);
+                    // 256 columns (eight waves, 64x64 each) where no tile straddles the k|v boundary
+                    if (g.seg_n % 256 == 0) return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 256, 2, 4, 2, 32>(gs, s);
                     return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s);
                 }
             }
