@@ -627,9 +627,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     // 44.8 us against 58.8 with the per-position tile (48.3 with 2x2 waves),
     // W_2 128x128 with 2 K groups 44.3 against 77.4, W_o 64x64 18.9 against
     // 25.6, W_kv 128x128 25.3 against 38.6. Then W_kv 128x256 with eight waves
-    // 22.9 / 25.6 against 24.9 / 28.0 for 128x128 (two boxes), and W_o's 64x64
-    // prefetching 2 K tiles 18.2 against 19.3 with 4; 256-row or 256-column
-    // tiles measured slower for W_1 (50.5-58.2) and W_2 (60.0-63.1).
+    // 22.9 / 25.6 against 24.9 / 28.0 for 128x128 (two boxes; eight side by
+    // side 23.7 against 24.5 for 2x4), W_o's 64x64 prefetching 2 K tiles 18.2
+    // against 19.3 with 4, W_2's K groups of four waves stacked (32x128 each)
+    // 47.4 against 50.2 for 2x2 (a slow box); 256-row or 256-column tiles
+    // measured slower for W_1 (50.5-58.2) and W_2 (60.0-63.1).
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1) {
@@ -682,7 +684,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
             }
             if constexpr (KS == 2) {
-                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32, 2>(gs, s);
+                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 4, 1, 2, 32, 2>(gs, s);
             }
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
@@ -704,8 +706,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             if constexpr (KS == 1) {
                 if (grouped) {
                     if (g.qkn_mask) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s);
-                    // 256 columns (eight waves, 64x64 each) where no tile straddles the k|v boundary
-                    if (g.seg_n % 256 == 0) return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 256, 2, 4, 2, 32>(gs, s);
+                    // 256 columns (eight waves side by side, 128x32 each) where no tile straddles the k|v boundary
+                    if (g.seg_n % 256 == 0) return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 256, 1, 8, 2, 32>(gs, s);
                     return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s);
                 }
             }

@@ -437,12 +437,17 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
                     }
                 }
             }
+            // this lane's half of the query's scores first: the two halves are
+            // combined (a cross-lane exchange) only when some lane's half would
+            // move the reference point; max(a, b)*sigma2 = max(a*sigma2, b*sigma2)
+            // exactly for sigma2 >= 0, so the decisions equal those on the whole row
             float mx = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sigma2;
-            const bool move = !(mx <= m_run + 8.0f);  // also true while m_run is -inf
-            if (__builtin_amdgcn_ballot_w64(move)) {
+            mx *= sigma2;
+            if (__builtin_amdgcn_ballot_w64(!(mx <= m_run + 8.0f))) {  // also true while m_run is -inf
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const bool move = !(mx <= m_run + 8.0f);
                 const float m_new = move ? fmaxf(m_run, mx) : m_run;
                 const float alpha = fast_exp2(m_run - m_new);
                 l_run *= alpha;
@@ -467,8 +472,7 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
                 p0[e] = (bf16)pa;
                 p1[e] = (bf16)pb;
             }
-            ps += __shfl_xor(ps, 32, 64);
-            l_run += ps;
+            l_run += ps;  // this lane's half of the row sum; the halves are added after the loop
             const bf16x8 vlo0 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(ql, c32 + 8 * g)]);
             const bf16x8 vlo1 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(ql, c32 + 8 * g + 16)]);
             const bf16x8 vhi0 = *reinterpret_cast<const bf16x8*>(&Vt[vt_at(32 + ql, c32 + 8 * g)]);
@@ -479,6 +483,7 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
             o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vhi1, p1, o1, 0, 0, 0);
         }
     }
+    l_run += __shfl_xor(l_run, 32, 64);  // the two halves of each query's row sum
     if (!qvalid) return;
 
     // this lane holds dh = blk*32 + 8*ee + 4*g + (0..3) for blk in {0,1}, ee in 0..3 (accumulator e = 4*ee + i)
