@@ -178,6 +178,43 @@ def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_t
     return np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)])  # ms
 
 
+def ceilings(dev):
+    """Achievable ceilings of this GPU, measured beside the product as reference
+    points for the roofline fractions (not part of the path): torch's device
+    copy of 2 GiB (read once, written once) and torch's bf16 product of two
+    8192 x 8192 matrices (hipBLASLt). Timed with events on torch's stream,
+    mean of 5 after 2."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def timed(f):
+        for _ in range(2):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 5 / 1e3
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * 2 * n / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    k = 8192
+    a = torch.randn((k, k), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((k, k), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((k, k), dtype=torch.bfloat16, device=dev)
+    gemm_tflops = 2.0 * k ** 3 / timed(lambda: torch.matmul(a, b, out=c)) / 1e12
+    del a, b, c
+    torch.cuda.synchronize()
+    log(f"ceilings: device copy {copy_gbs:.0f} GB/s, bf16 8192^3 product {gemm_tflops:.0f} TFLOP/s")
+    return {"copy_GB_s": round(copy_gbs, 1), "gemm_TFLOP_s": round(gemm_tflops, 1),
+            "measured": "torch device copy of 2 GiB (read + write); torch bf16 8192^3 matmul"}
+
+
 def update_only_bench(args, rt, wl):
     """The isolated blocked update (no layer around it): one step = the whole
     sequence's blocked attention with every pair known up front (rt_attn_forward:
@@ -243,6 +280,9 @@ def update_only_bench(args, rt, wl):
         cpu = {"value": round(len(rows) * N / cpu_s, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
                "kind": "oracle", "sample": f"{len(rows)} batch rows x all {N} positions ({cpu_s:.1f} s)"}
         log(f"cpu oracle: {cpu_s:.1f}s for the sample")
+    ceil = None if args.no_kernel_timing else ceilings(dev)
+    if ceil:
+        ceil["update_frac_of_copy"] = round(achieved / ceil["copy_GB_s"], 4)
     out = {
         "metric": "blocked-update tokens/s (isolated update, HBM GB/s)", "value": round(tokens_per_s, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -258,6 +298,7 @@ def update_only_bench(args, rt, wl):
                       "achieved_TFLOP_s": round(flops.sum() / (ms / 1e3) / 1e12, 1), "peak_TFLOP_s": 2500.0,
                       "frac": round(flops.sum() / (ms / 1e3) / 1e12 / 2500.0, 4)},
         "cpu_baseline": cpu,
+        "ceilings": ceil,
     }
     print(json.dumps(out), flush=True)
 
@@ -685,7 +726,10 @@ def main():
             "update_alg_GB_per_layer": round(float(byts.sum()) / 1e9, 3),
             "per_level": {str(b): {"steps": v[3], "us_per_step": round(v[0] / v[3] * 1e3, 2),
                                    "GB_s": round(v[1] / (v[0] / 1e3) / 1e9, 1),
-                                   "TFLOP_s": round(v[2] / (v[0] / 1e3) / 1e12, 2)}
+                                   "TFLOP_s": round(v[2] / (v[0] / 1e3) / 1e12, 2),
+                                   # max(bytes / HBM peak, flops / MFMA peak) over the measured time
+                                   "frac": round(max(v[1] / (v[0] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                                     v[2] / (v[0] / 1e3) / 1e12 / 2500.0), 4)}
                           for b, v in sorted(levels.items())},
         }
         log(f"update kernel: {achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of HBM peak), "
@@ -736,6 +780,10 @@ def main():
                         "peak_TFLOP_s": 2500.0, "frac": round(layer_tflops / 2500.0, 4)}
     if update_info:
         out["update"] = update_info
+        ceil = ceilings(dev)
+        ceil["update_frac_of_copy"] = round(roofline["achieved"] / ceil["copy_GB_s"], 4)
+        ceil["layer_mfma_frac_of_gemm"] = round(layer_tflops / ceil["gemm_TFLOP_s"], 4)
+        out["ceilings"] = ceil
     print(json.dumps(out), flush=True)
     for p in plans:
         p.destroy()
