@@ -178,6 +178,18 @@ def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_t
     return np.array([s_.elapsed_time(e_) for s_, e_ in zip(starts, ends)])  # ms
 
 
+def cpu_model():
+    """The host CPU's model name (Linux), for the oracle's timing."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def ceilings(dev):
     """Achievable ceilings of this GPU, measured beside the product as reference
     points for the roofline fractions (not part of the path): torch's device
@@ -660,17 +672,19 @@ def main():
         log(f"warmup {i + 1}/{args.warmup} done")
 
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the first and last bracket the timed region,
+    # the ones between give each step's time (their spread is reported)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     wall0 = time.time()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.time() - wall0
-    elapsed_ms = ev0.elapsed_time(ev1)
+    elapsed_ms = evs[0].elapsed_time(evs[-1])
     ms_per_step = elapsed_ms / args.steps
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
     tokens_per_s = B * N * args.steps / (elapsed_ms / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step (wall {wall / args.steps * 1e3:.2f} ms), "
         f"{tokens_per_s / 1e6:.3f} M tokens/s")
@@ -750,6 +764,7 @@ def main():
         cpu_value = len(rows) * npos / (cpu_s * L)
         span = f"all {N} positions" if npos == N else f"the first {npos} of {N} positions (later ones cost more)"
         cpu = {"value": round(cpu_value, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "cpu_model": cpu_model(), "nproc": os.cpu_count(),
                "sample": f"{len(rows)} batch rows x {span} x layer 1 of {L} "
                          f"({cpu_s:.1f} s); stack rate = rows*positions/({L}*time)"}
         log(f"cpu oracle: {cpu_s:.1f}s for the sample -> {cpu_value:.1f} stack tokens/s")
@@ -757,7 +772,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step_std": round(float(step_ms.std()), 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) inputs, N(0,1/d_in) weights)",
         "config": {"workload": f"{wl.name}: RT {L}-layer stack prefill x->z, bf16, B={B}, N={N}, d_model={D}, "
                                f"{H} heads x {dh}, MLP {F} GELU",
