@@ -14,6 +14,8 @@
 // epilogue (gemm.hip).
 #include <rocblas/rocblas.h>
 
+#include <mutex>
+
 #include "rt_device.h"
 #include "rt_internal.h"
 
@@ -310,7 +312,11 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 // W_bar^T (I x O) = U^T (I x R) * A_bar (R x O).
 
 namespace {
-rocblas_handle g_blas[64];  // one handle per device, created on first use
+// One handle per device, created on first use and kept until the process
+// ends. A handle's stream is state: the lock keeps each call's set-stream and
+// product together when several threads enqueue on one device.
+rocblas_handle g_blas[64];
+std::mutex g_blas_lock[64];
 }
 
 hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u, int64_t ldu, int64_t R, int O,
@@ -320,6 +326,7 @@ hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (R > 0x7fffffffLL || lda > 0x7fffffffLL || ldu > 0x7fffffffLL) return hipErrorInvalidValue;
+    std::lock_guard<std::mutex> hold(g_blas_lock[dev]);
     if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
         g_blas[dev] = nullptr;
         return hipErrorUnknown;

@@ -33,7 +33,10 @@
  *     rt_status, never thrown or aborted; rt_last_error() gives the text of
  *     the calling thread's last error.
  *   - The library allocates no device memory in any entry point except
- *     rt_layer_plan_create (which owns only its captured HIP graph).
+ *     plan creation (rt_layer_plan_create, rt_stack_plan_create: a plan owns
+ *     only its captured HIP graphs) and the first rt_layer_backward call on a
+ *     device, which creates that device's rocBLAS handle (rocBLAS's own device
+ *     workspace, kept until the process ends).
  */
 #ifndef RT_PREFILL_H
 #define RT_PREFILL_H
