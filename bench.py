@@ -570,6 +570,9 @@ def main():
                     help="attention backward of the blocked schedule at B=512, 16x64 heads, N=2048")
     ap.add_argument("--layer-backward", action="store_true",
                     help="the RT layer's backward at B=512, N=2048, d=1024 (one layer)")
+    ap.add_argument("--eager", action="store_true",
+                    help="enqueue the stack directly (rt_stack_forward, no graph): the same launches, for "
+                         "counter passes (rocprofv3's counter mode does not follow graph launches here)")
     ap.add_argument("--per-layer", action="store_true",
                     help="run the stack as one graph per layer, one after another (no layer wavefront)")
     ap.add_argument("--decode", action="store_true",
@@ -653,7 +656,9 @@ def main():
 
     t0 = time.time()
     plans = []
-    if args.per_layer:  # one graph per layer, replayed one after another
+    if args.eager:  # no graph: the same launches enqueued on every step
+        pass
+    elif args.per_layer:  # one graph per layer, replayed one after another
         for layer in range(L):
             xin = x if layer == 0 else zs[layer - 1]
             plans.append(rt.rt_layer_plan_create(desc, weights[layer], xin, zs[layer], ks[layer], vs[layer], ws))
@@ -663,6 +668,8 @@ def main():
     log(f"captured {len(plans)} graph(s) in {capture_s:.2f}s")
 
     def step():
+        if args.eager:
+            rt.rt_stack_forward(desc, weights, x, zs, ks, vs, ws, stream=stream)
         for p in plans:
             p.launch(stream)
 
@@ -778,7 +785,8 @@ def main():
                                f"{H} heads x {dh}, MLP {F} GELU",
                    "batch": B, "seq_len": N, "layers": L, "ms_per_layer": round(ms_per_step / L, 3),
                    "tokens_per_s_per_layer": round(tokens_per_s * L, 1), "graph_capture_s": round(capture_s, 2),
-                   "schedule": ("layer by layer, one graph each" if args.per_layer else
+                   "schedule": ("layer wavefront, eager launches (rt_stack_forward)" if args.eager else
+                                "layer by layer, one graph each" if args.per_layer else
                                 "layer wavefront, one graph (rt_stack_plan_create)"),
                    "parallelism": "single GPU"},
         "roofline": roofline,
