@@ -631,7 +631,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     // side 23.7 against 24.5 for 2x4), W_o's 64x64 prefetching 2 K tiles 18.2
     // against 19.3 with 4, W_2's K groups of four waves stacked (32x128 each)
     // 47.4 against 50.2 for 2x2 (a slow box); 256-row or 256-column tiles
-    // measured slower for W_1 (50.5-58.2) and W_2 (60.0-63.1).
+    // measured slower for W_1 (50.5-58.2) and W_2 (60.0-63.1). Eight waves per
+    // 128x128 tile (half the accumulators and prefetch registers per wave, twice
+    // the waves hiding the loads): W_1 4x2 waves (32x64 each, 128 VGPRs) 44.0
+    // against 56.4 for 1x4, W_2 2x4 waves without a K split (112 VGPRs) 40.9
+    // against 46.8 for two K groups of 4x1 (one box).
     switch (kind) {
         case GemmKind::QKV:
             if constexpr (KS == 1) {
@@ -671,7 +675,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (skinny) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 16, 32, 1, 1, D, 16, KS>(gs, s);
             }
             if constexpr (KS == 1) {
-                if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 1, 4, 2, 32>(gs, s);
+                if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 4, 2, 2, 32>(gs, s);
                 return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 64, 64, 2, 2, D, 16>(gs, s);
             }
@@ -682,9 +686,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
-            }
-            if constexpr (KS == 2) {
-                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 4, 1, 2, 32, 2>(gs, s);
+                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 4, 2, 32>(gs, s);
             }
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;
@@ -744,7 +746,7 @@ static int k_groups(GemmKind kind, const GemmArgs& g, int64_t max_m, int n) {
     int ks = kind == GemmKind::W2 ? 4
              : (kind == GemmKind::WO || kind == GemmKind::KV || kind == GemmKind::KV_UPDATE) ? 2
              : kind == GemmKind::PLAIN ? (g.K >= 4096 ? 4 : 2) : 1;  // W2_BWD: 12.1 us against 13.1 with 2
-    if (n >= 2 && kind != GemmKind::KV_UPDATE) ks = kind == GemmKind::W2 ? 2 : 1;  // several products per launch
+    if (n >= 2 && kind != GemmKind::KV_UPDATE) ks = 1;  // several products per launch (eight-wave tiles)
     if (n == 1 && max_m <= 16 && (kind == GemmKind::WO || kind == GemmKind::W1 || kind == GemmKind::W2 ||
                                   kind == GemmKind::KV))
         ks = kind == GemmKind::W2 ? 4 : 2;  // at most 16 rows
