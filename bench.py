@@ -59,9 +59,15 @@ def update_flops(t, n, p, dh):
     return 4 * dh * b * nq * p + 4 * dh * p  # block scores + PV, plus the ephemeral pair
 
 
-def measured_traffic():
+TRAFFIC_WORKLOAD = "stack6_d1024_b512_n2048"  # the workload whose update launches the counters measured
+
+
+def measured_traffic(workload):
     """HBM bytes per update launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
-    or None when the update kernel's source has changed since those counters were taken."""
+    or None for another workload's launches, or when the update kernel's source has changed
+    since those counters were taken."""
+    if workload != TRAFFIC_WORKLOAD:
+        return None
     import hashlib
     prof = os.path.join(ROOT, "profiles", "update_kernel_hbm_traffic_stack6_d1024_b512_n2048.txt")
     src = os.path.join(ROOT, "blocked_prefill_amd", "csrc", "update.hip")
@@ -729,7 +735,7 @@ def main():
         avg_s = graph_avg_s
         achieved = byts.mean() / avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
                     "kernel": "fused blocked update + finalize (update_small / update_simt / update_mfma kernels)",
                     "launches": N - 1, "avg_launch_us": round(avg_s * 1e6, 2),
                     "alg_bytes_per_launch": int(byts.mean())}

@@ -51,3 +51,10 @@ def test_update_bytes_at_the_stack_layer_shape():
     total = sum(bench.update_bytes(t, n, p, 64, 2) for t in range(1, n))
     assert total == 81_739_776_000
     assert int(total / (n - 1)) == 39_931_497
+
+
+def test_measured_traffic_belongs_to_its_workload():
+    """The committed counters were taken on the stack's layer shape: no other
+    workload reports them."""
+    assert bench.measured_traffic("layer_d768_b512_n1024") is None
+    assert bench.measured_traffic("long_d1024_b8_n32768") is None
