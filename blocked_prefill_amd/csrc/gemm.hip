@@ -728,6 +728,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
             break;
         case GemmKind::W2_BWD:
+            if constexpr (KS == 1) {  // 128x64 with eight waves: 11.1 us against 12.0 for 64x64 (M = 512)
+                if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 128, 64, 4, 2, 2, 32>(gs, s);
+            }
             if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(gs, s);
             break;
         case GemmKind::PLAIN:
@@ -737,6 +740,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             // per-position adjoint products (M = 512, N = 1024): 64x32 tiles, twice the
             // workgroups of 64x64 (K = 1024: 6.1 against 6.9 us, 2048: 8.6 against 9.9,
             // 4096: 14.1 against 17.6)
+            if constexpr (KS <= 2) {  // 2x2 waves per K group: 5.6 / 8.0 us against 6.1 / 8.7 (K = 1024 / 2048)
+                if (!big) return run_pipe<float, float, 0, 64, 32, 2, 2, D, 16, KS>(gs, s);
+            }
             if (!big) return run_pipe<float, float, 0, 64, 32, 2, 1, D, 16, KS>(gs, s);
             break;
     }
