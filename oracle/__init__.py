@@ -31,7 +31,7 @@ class _Cfg(ctypes.Structure):
                 ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_double), ("residual_scale", ctypes.c_double),
                 ("rms_eps", ctypes.c_double), ("kv_from_input", ctypes.c_int32),
-                ("round_bf16", ctypes.c_int32), ("qk_norm", ctypes.c_int32)]
+                ("round_bf16", ctypes.c_int32), ("qk_norm", ctypes.c_int32), ("kv_source_norm", ctypes.c_int32)]
 
 
 class _Weights(ctypes.Structure):
@@ -82,10 +82,26 @@ def _f32(a):
 
 
 def round_bf16(v: np.ndarray) -> np.ndarray:
-    """Round each value (float64) to the nearest bf16, ties to even."""
-    f = lib().rto_round_bf16
+    """Round each value (float64) to the nearest bf16, ties to even.
+
+    The same definition as rto_round_bf16 in rt_oracle.c (8 significant bits,
+    the binary32 exponent range with its subnormal spacing 2^-133, overflow to
+    infinity), vectorised over the array.
+    """
     v = np.asarray(v, dtype=np.float64)
-    return np.array([f(float(x)) for x in v.ravel()], dtype=np.float64).reshape(v.shape)
+    a = np.abs(v)
+    _, e = np.frexp(a)                                   # a = f * 2^e, f in [0.5, 1)
+    ulp_exp = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(a, -ulp_exp)), ulp_exp)  # np.rint: ties to even
+    r = np.where(r > np.ldexp(255.0, 120), np.inf, r)
+    out = np.copysign(r, v)
+    keep = (a == 0) | ~np.isfinite(v)
+    return np.where(keep, v, out)
+
+
+def round_bf16_scalar(x: float) -> float:
+    """rto_round_bf16 of rt_oracle.c on one value."""
+    return float(lib().rto_round_bf16(float(x)))
 
 
 def gelu(u: np.ndarray) -> np.ndarray:
@@ -155,13 +171,15 @@ def attention_at(q, k_eph, v_eph, k, v, softmax_scale: float, positions) -> np.n
 
 def layer_forward(x, weights: dict, *, n_heads: int, softmax_scale: float, residual_scale: float = 1.0,
                   rms_eps: float = 1e-6, kv_from_input: bool = False, round_bf16: bool = False,
-                  qk_norm: bool = False, want=("z", "k", "v")) -> dict:
+                  qk_norm: bool = False, kv_source_norm: bool = True, want=("z", "k", "v")) -> dict:
     """Naive RT layer on x [N][R][d] (fp32 values). Returns float64 outputs by name.
 
     Names: z, k, v, q, k_eph, v_eph, a, h ([N][R][d]); g ([N][R][F]); and
     always x_next (float32, z as stored: the next layer's input).
     qk_norm: every query and key RMS-normalised per head (gains g_q, g_k of the
     weights, ones when absent).
+    kv_source_norm: the persistent pair is W_{k,v} RMS_attn(z_t) (True) or
+    W_{k,v} z_t (False, the literal reading of the cut formula).
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
     N, R, d = x.shape
@@ -169,7 +187,7 @@ def layer_forward(x, weights: dict, *, n_heads: int, softmax_scale: float, resid
     if d % n_heads:
         raise ValueError("d_model must be a multiple of n_heads")
     cfg = _Cfg(N, R, d, n_heads, d // n_heads, F, softmax_scale, residual_scale, rms_eps,
-               int(bool(kv_from_input)), int(bool(round_bf16)), int(bool(qk_norm)))
+               int(bool(kv_from_input)), int(bool(round_bf16)), int(bool(qk_norm)), int(bool(kv_source_norm)))
     keep = {}
     wp = {}
     for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp", "g_q", "g_k"):

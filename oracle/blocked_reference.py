@@ -71,9 +71,10 @@ def attention(q, k_eph, v_eph, k, v, softmax_scale):
 
 
 def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1e-6, kv_from_input=False,
-                  qk_norm=False):
+                  qk_norm=False, kv_source_norm=True):
     """Blocked-schedule RT layer in float64 on x [N][R][d]. Returns z, k, v (float64).
-    qk_norm: queries and keys RMS-normalised per head (gains g_q, g_k)."""
+    qk_norm: queries and keys RMS-normalised per head (gains g_q, g_k).
+    kv_source_norm=False: the persistent pair is W_{k,v} z_t, without the RMS."""
     x = np.asarray(x, dtype=np.float64)
     n, rows, d = x.shape
     dh = d // n_heads
@@ -99,7 +100,7 @@ def layer_forward(x, w, *, n_heads, softmax_scale, residual_scale=1.0, rms_eps=1
         h = x[i] + rho * a @ W["w_o"].T
         z[i] = h + rho * _gelu(_rms(h, g_mlp, rms_eps) @ W["w_1"].T) @ W["w_2"].T
         src = x[i] if kv_from_input else z[i]
-        us = _rms(src, g_attn, rms_eps)
+        us = _rms(src, g_attn, rms_eps) if (kv_from_input or kv_source_norm) else src
         K[i] = head_rms((us @ W["w_k"].T).reshape(rows, n_heads, dh), g_k)
         V[i] = (us @ W["w_v"].T).reshape(rows, n_heads, dh)
         (k0, k1), (q0, q1) = step(t, n)

@@ -24,7 +24,10 @@
  * The oracle runs exactly that naive schedule. Where the pages leave a step
  * open, the readings taken are:
  *   - the persistent pair is k_t = W_k RMS(z_t), v_t = W_v RMS(z_t), the same
- *     function that forms the ephemeral pair, applied to the output;
+ *     function that forms the ephemeral pair, applied to the output
+ *     (kv_source_norm = 1); the text of section 2.2 breaks off before this
+ *     formula, and with kv_source_norm = 0 the oracle takes the literal
+ *     reading k_t = W_k z_t, v_t = W_v z_t instead;
  *   - scores are scaled by a softmax scale sigma (the pages write none and
  *     use query/key normalisation instead; sigma = 1/sqrt(head_dim) is used
  *     by the workloads, sigma = 1 gives the written operator);
@@ -336,6 +339,7 @@ typedef struct {
     int32_t kv_from_input; /* 0: persistent pair from z_t (RT); 1: from x_t (Transformer) */
     int32_t round_bf16;    /* round the stored tensors to bf16 */
     int32_t qk_norm;       /* RMS-normalise each head's query and key (ephemeral and persistent) */
+    int32_t kv_source_norm;/* RT: 1 the persistent pair reads RMS_attn(z_t); 0 it reads z_t itself */
 } rto_layer_cfg;
 
 typedef struct {
@@ -371,7 +375,8 @@ static void put(double* dst, size_t off, const double* src, int n) {
  *   h      = x_t + rho W_o a
  *   z_t    = h + rho W_2 GELU(W_1 RMS_mlp(h))
  *   k_t, v_t = W_k RMS_attn(z_t), W_v RMS_attn(z_t)   (from x_t instead when
- *            kv_from_input is set, which is the standard Transformer layer)
+ *            kv_from_input is set, which is the standard Transformer layer;
+ *            W_k z_t, W_v z_t when kv_source_norm is 0)
  * With qk_norm, every query and key (q, k', k) is RMS-normalised per head
  * after its projection, with gains g_q, g_k (the "magenta" RMS of the
  * translated paper's section 2 notation, read per head as in the query/key
@@ -507,7 +512,7 @@ int rto_layer_forward(const rto_layer_cfg* c, const rto_weights* w, const float*
                 out->x_next[(size_t)t * Rd + (size_t)r * d + i] = (float)zv;
                 zs[i] = c->kv_from_input ? b[i] : zv;
             }
-            rto_rmsnorm(zs, d, w->g_attn, eps, zs);
+            if (c->kv_from_input || c->kv_source_norm) rto_rmsnorm(zs, d, w->g_attn, eps, zs);
         }
 #pragma omp parallel for schedule(static)
         for (int o = 0; o < 2 * d; ++o) {

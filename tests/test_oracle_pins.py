@@ -297,3 +297,60 @@ def test_bf16_emulation_stores_bf16_values_and_stays_close():
     assert np.array_equal(xs, oracle.round_bf16(emu["z"]))
     assert _rel(emu["z"], ref["z"]) < 2e-2
     assert _rel(emu["z"], ref["z"]) > 0.0
+
+
+@pytest.mark.parametrize("n,qk", [(1, False), (8, False), (37, False), (20, True)])
+def test_literal_kv_source_blocked_equals_naive(n, qk):
+    """The literal reading of the cut persistent-pair formula (translated paper
+    section 2.2): k_t = W_k z_t, v_t = W_v z_t without the RMS; the blocked
+    schedule reaches the naive result there too."""
+    rng = _rng(80 + n)
+    d, h, f, r = 32, 2, 64, 2
+    x = rng.standard_normal((n, r, d)).astype(np.float32)
+    w = _weights(rng, d, f)
+    if qk:
+        w["g_q"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+        w["g_k"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    kw = dict(n_heads=h, softmax_scale=0.3, residual_scale=0.8, qk_norm=qk, kv_source_norm=False)
+    got = oracle.layer_forward(x, w, **kw)
+    want = blocked.layer_forward(x, w, **kw)
+    for name in ("z", "k", "v"):
+        assert _rel(got[name], want[name]) <= 1e-12, name
+    if n > 1:
+        normed = oracle.layer_forward(x, w, **dict(kw, kv_source_norm=True))
+        assert _rel(got["z"], normed["z"]) > 1e-3  # the two readings differ
+
+
+def test_literal_kv_source_reads_the_output_itself():
+    """W_q = 0 (uniform weights): position 2's output is the mean of W_v z_1, the
+    value built from the first position's output with no RMS, and of its own
+    ephemeral value W_v RMS_attn(x_2)."""
+    rng = _rng(31)
+    d, h, f = 32, 4, 64
+    x = rng.standard_normal((2, 1, d)).astype(np.float32)
+    w = _weights(rng, d, f)
+    w["w_q"] = np.zeros_like(w["w_q"])
+    eps = 1e-6
+    got = oracle.layer_forward(x, w, n_heads=h, softmax_scale=0.125, rms_eps=eps, kv_source_norm=False,
+                               want=("z", "a", "v", "k"))
+    Wt = {k: torch.from_numpy(v.astype(np.float64)) for k, v in w.items()}
+    z1 = torch.from_numpy(got["z"][0, 0])
+    v1 = F.linear(z1, Wt["w_v"])
+    v2e = F.linear(F.rms_norm(torch.from_numpy(x[1, 0].astype(np.float64)), (d,), weight=Wt["g_attn"], eps=eps),
+                   Wt["w_v"])
+    assert _rel(got["v"][0, 0], v1.numpy()) < 1e-13
+    assert _rel(got["k"][0, 0], F.linear(z1, Wt["w_k"]).numpy()) < 1e-13
+    assert _rel(got["a"][1, 0], ((v1 + v2e) / 2).numpy()) < 1e-13
+    # z_1 does not depend on the reading (position 1 sees only its own pair)
+    first = _textbook_transformer_layer(x[:1], w, h, 0.125, 1.0, eps)
+    assert _rel(got["z"][0], first["z"][0]) < 1e-13
+
+
+def test_round_bf16_vector_and_c_forms_agree():
+    """The oracle's vectorised rounding and its C form (used inside the layer) agree."""
+    rng = _rng(2)
+    v = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-45, 40, 3000),
+                        np.array([0.0, -0.0, np.inf, -np.inf, 3.3961e38, 1e-45, 2.0 ** -134, 2.0 ** -133 * 1.5])])
+    got = oracle.round_bf16(v)
+    want = np.array([oracle.round_bf16_scalar(x) for x in v])
+    assert np.array_equal(got, want)
