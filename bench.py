@@ -30,6 +30,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "RT layer prefill tokens/s at B=512 + blocked-update HBM GB/s / MFMA util"
 HBM_PEAK_GBS = 8000.0
+# the oracle timed as the CPU baseline, as it stands (oracle/build.py)
+ORACLE_BUILD = ("oracle/rt_oracle.c, naive schedule, IEEE fp64 with bf16 storage emulation; "
+                "gcc -O3 -ffp-contract=off -fopenmp, no -march flags; one OpenMP thread per core")
 
 
 def log(msg):
@@ -196,12 +199,27 @@ def cpu_model():
     return "unknown"
 
 
+def stream_probe():
+    """The bandwidth probes' library (blocked_prefill_amd/librt_probe.so), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "blocked_prefill_amd", "librt_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.rt_probe_stream.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                            ctypes.c_void_p]
+    lib.rt_probe_stream.restype = ctypes.c_int
+    return lib
+
+
 def ceilings(dev):
     """Achievable ceilings of this GPU, measured beside the product as reference
     points for the roofline fractions (not part of the path): torch's device
-    copy of 2 GiB (read once, written once) and torch's bf16 product of two
-    8192 x 8192 matrices (hipBLASLt). Timed with events on torch's stream,
-    mean of 5 after 2."""
+    copy of 2 GiB (read once, written once); the library's streaming probe with
+    three 1 GiB streams read and one written (the blocked update's ~3:1
+    read:write mix) and with one read and one written; and torch's bf16
+    product of two 8192 x 8192 matrices (hipBLASLt). Timed with events on
+    torch's stream, mean of 5 after 2."""
     import torch
     stream = torch.cuda.current_stream()
 
@@ -221,6 +239,20 @@ def ceilings(dev):
     dst = torch.empty_like(src)
     copy_gbs = 2 * 2 * n / timed(lambda: dst.copy_(src)) / 1e9
     del src, dst
+    probe = stream_probe()
+    stream_gbs = {}
+    if probe is not None:
+        n16 = (1 << 30) // 16
+        bufs = [torch.empty(1 << 30, dtype=torch.uint8, device=dev) for _ in range(4)]
+        for b_ in bufs:
+            b_.fill_(7)
+        ptr = [b_.data_ptr() for b_ in bufs]
+        for reads in (3, 1):
+            def run(reads=reads):
+                rc = probe.rt_probe_stream(ptr[0], ptr[1], ptr[2], ptr[3], n16, reads, 0, stream.cuda_stream)
+                assert rc == 0, rc
+            stream_gbs[reads] = (reads + 1) * (1 << 30) / timed(run) / 1e9
+        del bufs
     k = 8192
     a = torch.randn((k, k), dtype=torch.bfloat16, device=dev)
     b = torch.randn((k, k), dtype=torch.bfloat16, device=dev)
@@ -228,9 +260,13 @@ def ceilings(dev):
     gemm_tflops = 2.0 * k ** 3 / timed(lambda: torch.matmul(a, b, out=c)) / 1e12
     del a, b, c
     torch.cuda.synchronize()
-    log(f"ceilings: device copy {copy_gbs:.0f} GB/s, bf16 8192^3 product {gemm_tflops:.0f} TFLOP/s")
-    return {"copy_GB_s": round(copy_gbs, 1), "gemm_TFLOP_s": round(gemm_tflops, 1),
-            "measured": "torch device copy of 2 GiB (read + write); torch bf16 8192^3 matmul"}
+    log(f"ceilings: device copy {copy_gbs:.0f} GB/s, streams 3:1 {stream_gbs.get(3, 0):.0f} GB/s, "
+        f"1:1 {stream_gbs.get(1, 0):.0f} GB/s, bf16 8192^3 product {gemm_tflops:.0f} TFLOP/s")
+    return {"copy_GB_s": round(copy_gbs, 1), "stream_3r1w_GB_s": round(stream_gbs.get(3, 0.0), 1),
+            "stream_1r1w_GB_s": round(stream_gbs.get(1, 0.0), 1), "gemm_TFLOP_s": round(gemm_tflops, 1),
+            "measured": "torch device copy of 2 GiB (read + write); the library's streaming probe, three "
+                        "1 GiB streams read and one written, and one read and one written; torch bf16 "
+                        "8192^3 matmul"}
 
 
 def update_only_bench(args, rt, wl):
@@ -290,17 +326,20 @@ def update_only_bench(args, rt, wl):
         f"{achieved:.0f} GB/s algorithmic ({achieved / HBM_PEAK_GBS:.1%} of HBM peak)")
     cpu = None
     if not args.no_cpu:
-        rows = list(range(min(args.cpu_rows, B)))
+        rows = list(range(min(args.cpu_rows or oracle.num_threads(), B)))
         tr = rt_inputs.attn_inputs(wl, rows=rows)
         t0 = time.time()
         oracle.attention(tr["q"], tr["k_eph"], tr["v_eph"], tr["k"], tr["v"], scale)
         cpu_s = time.time() - t0
         cpu = {"value": round(len(rows) * N / cpu_s, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "sample": f"{len(rows)} batch rows x all {N} positions ({cpu_s:.1f} s)"}
+               "kind": "oracle", "build": ORACLE_BUILD,
+               "sample": f"{len(rows)} batch rows x all {N} positions ({cpu_s:.1f} s)"}
         log(f"cpu oracle: {cpu_s:.1f}s for the sample")
     ceil = None if args.no_kernel_timing else ceilings(dev)
     if ceil:
         ceil["update_frac_of_copy"] = round(achieved / ceil["copy_GB_s"], 4)
+        if ceil["stream_3r1w_GB_s"]:
+            ceil["update_frac_of_stream_3r1w"] = round(achieved / ceil["stream_3r1w_GB_s"], 4)
     out = {
         "metric": "blocked-update tokens/s (isolated update, HBM GB/s)", "value": round(tokens_per_s, 1),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -560,7 +599,8 @@ def main():
     ap.add_argument("--workload", default="stack6_d1024_b512_n2048")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-kernel-timing", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="batch rows of the CPU-oracle sample (0: one per oracle thread)")
     ap.add_argument("--cpu-positions", type=int, default=0,
                     help="CPU sample: the first P positions only (default: all, or 2048 when N > 8192; "
                          "outputs at positions <= P depend on those positions only)")
@@ -765,7 +805,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        rows = list(range(min(args.cpu_rows, B)))
+        rows = list(range(min(args.cpu_rows or oracle.num_threads(), B)))
         # long sequences: a prefix keeps the naive oracle (quadratic in N) within seconds
         npos = args.cpu_positions if 0 < args.cpu_positions < N else (2048 if N > 8192 else N)
         xr = rt_inputs.layer_input(wl, rows=rows)[:npos]
@@ -777,7 +817,7 @@ def main():
         cpu_value = len(rows) * npos / (cpu_s * L)
         span = f"all {N} positions" if npos == N else f"the first {npos} of {N} positions (later ones cost more)"
         cpu = {"value": round(cpu_value, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+               "build": ORACLE_BUILD, "cpu_model": cpu_model(), "nproc": os.cpu_count(),
                "sample": f"{len(rows)} batch rows x {span} x layer 1 of {L} "
                          f"({cpu_s:.1f} s); stack rate = rows*positions/({L}*time)"}
         log(f"cpu oracle: {cpu_s:.1f}s for the sample -> {cpu_value:.1f} stack tokens/s")
@@ -811,6 +851,10 @@ def main():
         out["update"] = update_info
         ceil = ceilings(dev)
         ceil["update_frac_of_copy"] = round(roofline["achieved"] / ceil["copy_GB_s"], 4)
+        if ceil["stream_3r1w_GB_s"]:
+            ceil["update_frac_of_stream_3r1w"] = round(roofline["achieved"] / ceil["stream_3r1w_GB_s"], 4)
+            for v in out["update"]["per_level"].values():
+                v["frac_of_stream_3r1w"] = round(v["GB_s"] / ceil["stream_3r1w_GB_s"], 4)
         ceil["layer_mfma_frac_of_gemm"] = round(layer_tflops / ceil["gemm_TFLOP_s"], 4)
         out["ceilings"] = ceil
     print(json.dumps(out), flush=True)

@@ -52,7 +52,12 @@ class AttnDesc(ctypes.Structure):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("attn", AttnDesc), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("residual_scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+                ("rms_eps", ctypes.c_float), ("residual_scale", ctypes.c_float), ("kv_source_norm", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+    def __init__(self, *args, kv_source_norm: int = 1, **kw):
+        # 1 (the persistent pair reads RMS_attn(z_t)) unless the caller says otherwise
+        super().__init__(*args, kv_source_norm=kv_source_norm, **kw)
 
 
 class LayerWeights(ctypes.Structure):

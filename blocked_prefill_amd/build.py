@@ -11,6 +11,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "librt_prefill.so")
+PROBE = os.path.join(HERE, "librt_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -53,10 +54,13 @@ def build(verbose: bool = False) -> str:
         with ThreadPoolExecutor(workers) as ex:
             for f in [ex.submit(_run, cmd, verbose) for _, _, cmd in jobs]:
                 f.result()
-        # rocBLAS: the backward's weight gradients (plain GEMMs reducing over positions x rows)
-        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *[o for _, o, _ in jobs], "-lrocblas",
-              "-o", LIB + ".tmp"], verbose)
+        _run([HIPCC, "--offload-arch=gfx950", "-fPIC", "-shared", *[o for _, o, _ in jobs], "-o", LIB + ".tmp"],
+             verbose)
     os.replace(LIB + ".tmp", LIB)
+    # the benchmark's bandwidth probes (a separate library: not part of the layer's path)
+    _run([HIPCC, *COMMON, "-shared", os.path.join(HERE, "probe", "stream_ceiling.hip"), "-o", PROBE + ".tmp"],
+         verbose)
+    os.replace(PROBE + ".tmp", PROBE)
     return LIB
 
 

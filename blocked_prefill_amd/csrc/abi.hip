@@ -71,6 +71,10 @@ rt_status check_layer(const rt_layer_desc* d) {
         return fail(RT_ERR_UNSUPPORTED, "the bf16 query/key norm supports head_dim 32 or 64");
     if (d->attn.dtype == RT_BF16 && d->d_model > 64 * rt::kRowSSTile)
         return fail(RT_ERR_UNSUPPORTED, "bf16 layers support d_model up to %d", 64 * rt::kRowSSTile);
+    if (d->kv_source_norm != 0 && d->kv_source_norm != 1)
+        return fail(RT_ERR_INVALID_ARG, "kv_source_norm must be 0 or 1 (got %d)", d->kv_source_norm);
+    if (!d->kv_source_norm && (d->flags & RT_FLAG_TRANSFORMER))
+        return fail(RT_ERR_INVALID_ARG, "the Transformer layer's pair is its ephemeral pair: kv_source_norm must be 1");
     return RT_OK;
 }
 
@@ -99,7 +103,7 @@ struct Layout {
     size_t g;             // [rows][F] dtype: MLP hidden activation
     size_t hb;            // [rows][d] bf16: h rounded, the MLP's first operand (bf16 layers)
     size_t hss, zss;      // [rows][d/32] fp32: partial row sums of h^2 and of z^2 (bf16 layers)
-    size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given)
+    size_t wq, wk, wv, w1;// gain-folded weights (used when gains are given; bf16: two halves per row)
     size_t xss;           // [N*B][4] fp32: quarter-row sums of x^2 (bf16 layers: the up-front RMS)
     size_t total;
 };
@@ -132,10 +136,11 @@ Layout layout_of(const rt_layer_desc* d, Mode mode) {
     L.hb = take(rows * D * 2);
     L.hss = take(D / rt::kRowSSTile * rows * 4 + 4);
     L.zss = take(D / rt::kRowSSTile * rows * 4 + 4);
-    L.wq = take(D * D * es);
-    L.wk = take(D * D * es);
-    L.wv = take(D * D * es);
-    L.w1 = take(F * D * es);
+    const size_t halves = d->attn.dtype == RT_BF16 ? 2 : 1;  // a bf16 folded weight is stored in two halves
+    L.wq = take(halves * D * D * es);
+    L.wk = take(halves * D * D * es);
+    L.wv = take(halves * D * D * es);
+    L.w1 = take(halves * F * D * es);
     L.xss = take(N * B * 16);
     L.total = off;
     return L;
@@ -199,9 +204,12 @@ rt_status check_layer_ptrs(const rt_layer_weights* w, const void* x, void* z, vo
 }
 
 // The projections each RMS normalisation feeds, with the gain folded in
-// (W'[r][c] = W[r][c] g[c]) when a gain is given.
+// (W'[r][c] = W[r][c] g[c]) when a gain is given. A bf16 folded weight holds
+// two bf16 halves per row (launch_fold_gain), so its products run over
+// kq (or k1) = 2 d columns, each A row read twice.
 struct Projections {
     const void *wq, *wk, *wv, *w1;
+    int32_t kq, k1;  // K of the products with W_q, W_k, W_v and with W_1
 };
 
 rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* base, const Layout& L,
@@ -210,7 +218,8 @@ rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* 
     const rt_dtype dt = d->attn.dtype;
     const int32_t D = d->d_model, F = d->d_ff;
     hipStream_t s = run.s;
-    *p = Projections{w->w_q, w->w_k, w->w_v, w->w_1};
+    const int32_t halves = dt == RT_BF16 ? 2 : 1;
+    *p = Projections{w->w_q, w->w_k, w->w_v, w->w_1, D, D};
     if (w->g_attn) {
         RT_TRY(run.check(launch_fold_gain(dt, w->w_q, w->g_attn, base + L.wq, D, D, s), "fold g_attn"));
         RT_TRY(run.check(launch_fold_gain(dt, w->w_k, w->g_attn, base + L.wk, D, D, s), "fold g_attn"));
@@ -218,10 +227,12 @@ rt_status enqueue_fold(const rt_layer_desc* d, const rt_layer_weights* w, char* 
         p->wq = base + L.wq;
         p->wk = base + L.wk;
         p->wv = base + L.wv;
+        p->kq = halves * D;
     }
     if (w->g_mlp) {
         RT_TRY(run.check(launch_fold_gain(dt, w->w_1, w->g_mlp, base + L.w1, F, D, s), "fold g_mlp"));
         p->w1 = base + L.w1;
+        p->k1 = halves * D;
     }
     return RT_OK;
 }
@@ -241,7 +252,7 @@ rt::GemmArgs qkv_args(const rt_layer_desc* d, const rt_layer_weights* w, const P
     gq.W[0] = p.wq; gq.W[1] = p.wk; gq.W[2] = p.wv;
     gq.C[0] = q; gq.C[1] = ke; gq.C[2] = ve;
     gq.ldc = D; gq.seg_n = D; gq.eps = d->rms_eps;
-    gq.M = rows; gq.N = 3 * D; gq.K = D;
+    gq.M = rows; gq.N = 3 * D; gq.K = p.kq; gq.a_k = D;
     if (d->flags & RT_FLAG_QK_NORM) {
         gq.qkn_mask = 3; gq.head_dim = d->attn.head_dim;
         gq.qkn_gain[0] = w->g_q; gq.qkn_gain[1] = w->g_k;
@@ -289,7 +300,7 @@ TailArgs tail_args(const rt_layer_desc* d, const rt_layer_weights* w, const Proj
 
     GemmArgs& g1 = ta.w1;  // g = GELU(W_1 RMS_mlp(h))
     g1.A = b16 ? (const void*)(base + L.hb) : (const void*)h; g1.lda = D; g1.W[0] = p.w1; g1.C[0] = g;
-    g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = rows; g1.N = F; g1.K = D;
+    g1.ldc = F; g1.seg_n = F; g1.eps = d->rms_eps; g1.M = rows; g1.N = F; g1.K = p.k1; g1.a_k = D;
     if (b16) { g1.rss_in = (const float*)(base + L.hss); g1.n_parts = parts; }
 
     GemmArgs& g2 = ta.w2;  // z = h + rho W_2 g
@@ -300,8 +311,11 @@ TailArgs tail_args(const rt_layer_desc* d, const rt_layer_weights* w, const Proj
     if (kt) {
         GemmArgs& gk = ta.kv;  // persistent pair from the output z
         gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = kt; gk.C[1] = vt;
-        gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = D;
+        gk.ldc = D; gk.seg_n = D; gk.eps = d->rms_eps; gk.M = rows; gk.N = 2 * D; gk.K = p.kq; gk.a_k = D;
         if (b16) { gk.rss_in = (const float*)(base + L.zss); gk.n_parts = parts; }
+        if (!d->kv_source_norm) {  // the literal reading: W_k z_t, W_v z_t (the weights without g_attn)
+            gk.W[0] = w->w_k; gk.W[1] = w->w_v; gk.K = D; gk.no_rms = 1;
+        }
         if (d->flags & RT_FLAG_QK_NORM) { gk.qkn_mask = 1; gk.head_dim = d->attn.head_dim; gk.qkn_gain[0] = w->g_k; }
     }
     return ta;
@@ -661,6 +675,7 @@ rt_status check_backward(const rt_layer_desc* d) {
     RT_TRY(check_layer(d));
     if (d->flags & RT_FLAG_TRANSFORMER) return fail(RT_ERR_UNSUPPORTED, "the backward covers the RT layer only");
     if (d->flags & RT_FLAG_QK_NORM) return fail(RT_ERR_UNSUPPORTED, "the backward does not cover RT_FLAG_QK_NORM");
+    if (!d->kv_source_norm) return fail(RT_ERR_UNSUPPORTED, "the backward covers kv_source_norm = 1 only");
     return RT_OK;
 }
 
@@ -684,6 +699,8 @@ struct BLayout {
     size_t qkvb, kvb;                      // [NB][3d], [NB][2d] dtype: adjoints as product operands
     size_t gpart;                          // gain-gradient partial sums
     size_t xss;                            // [NB][4] fp32: quarter-row sums of x^2
+    size_t wta, wtu, wpart;                // weight gradients: transposed operands and split partials
+    int64_t wrows;                         // rows of the transposed operands (NB padded)
     size_t total;
 };
 
@@ -698,7 +715,9 @@ BLayout blayout_of(const rt_layer_desc* d) {
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
-    L.wq = take(D * D * es); L.wk = take(D * D * es); L.wv = take(D * D * es); L.w1 = take(F * D * es);
+    const size_t halves = d->attn.dtype == RT_BF16 ? 2 : 1;  // folded bf16 weights: two halves per row
+    L.wq = take(halves * D * D * es); L.wk = take(halves * D * D * es); L.wv = take(halves * D * D * es);
+    L.w1 = take(halves * F * D * es);
     L.wkvT = take(D * 2 * D * es); L.w2T = take(F * D * es); L.w1T = take(D * F * es); L.woT = take(D * D * es);
     L.wqkvT = take(D * 3 * D * es);
     L.q = take(NB * D * es); L.ke = take(NB * D * es); L.ve = take(NB * D * es);
@@ -721,6 +740,13 @@ BLayout blayout_of(const rt_layer_desc* d) {
     L.kvb = take(NB * 2 * D * es);
     L.gpart = take((size_t)rt::gain_grad_blocks((int64_t)NB) * D * 4);
     L.xss = take(NB * 16);
+    const rt::WgradPlan wp = rt::wgrad_plan((int64_t)NB);
+    const size_t maxO = 3 * D > F ? 3 * D : F, maxI = D > F ? D : F;
+    L.wrows = wp.rows_pad;
+    L.wta = take(maxO * (size_t)wp.rows_pad * es);
+    L.wtu = take(maxI * (size_t)wp.rows_pad * es);
+    L.wpart = take((size_t)wp.splits * D * F * 4 > (size_t)wp.splits * 3 * D * D * 4 ? (size_t)wp.splits * D * F * 4
+                                                                                      : (size_t)wp.splits * 3 * D * D * 4);
     L.total = off;
     return L;
 }
@@ -761,7 +787,7 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
     {   // the persistent pairs from the stored outputs
         GemmArgs gk{};
         gk.A = z; gk.lda = D; gk.W[0] = p.wk; gk.W[1] = p.wv; gk.C[0] = at(L.kc); gk.C[1] = at(L.vc);
-        gk.ldc = D; gk.seg_n = D; gk.eps = eps; gk.M = NB; gk.N = 2 * D; gk.K = D;
+        gk.ldc = D; gk.seg_n = D; gk.eps = eps; gk.M = NB; gk.N = 2 * D; gk.K = p.kq; gk.a_k = D;
         RT_TRY(run.check(launch_gemm(dt, GemmKind::QKV, gk, s), "persistent pairs from z"));
     }
     {   // the blocked attention with each query's log-sum-exp (finishing query t+1 in step t)
@@ -779,7 +805,7 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
         RT_TRY(run.check(launch_gemm(dt, GemmKind::WO, go, s), "h recompute"));
         GemmArgs g1{};  // u = W_1 RMS_mlp(h), before the GELU
         g1.A = b16 ? at(L.hb) : (const void*)f32(L.h); g1.lda = D; g1.W[0] = p.w1; g1.C[0] = at(L.u);
-        g1.ldc = F; g1.seg_n = F; g1.eps = eps; g1.M = NB; g1.N = F; g1.K = D;
+        g1.ldc = F; g1.seg_n = F; g1.eps = eps; g1.M = NB; g1.N = F; g1.K = p.k1; g1.a_k = D;
         if (b16) { g1.rss_in = f32(L.hss); g1.n_parts = D / kRowSSTile; }
         RT_TRY(run.check(launch_gemm(dt, GemmKind::W1_PRE, g1, s), "u recompute"));
     }
@@ -865,14 +891,21 @@ rt_status enqueue_layer_backward(const rt_layer_desc* d, const rt_layer_weights*
     RT_TRY(run.check(launch_gelu_inplace(dt, at(L.u), NB * F, s), "GELU(u)"));
     const char* qkvb = base + L.qkvb;
     const char* kvb = base + L.kvb;
-    RT_TRY(run.check(weight_grad(dt, qkvb, 3 * D, ux, D, NB, D, D, gr->w_q, false, s), "W_q gradient"));
-    RT_TRY(run.check(weight_grad(dt, qkvb + D * es, 3 * D, ux, D, NB, D, D, gr->w_k, false, s), "W_k gradient"));
-    RT_TRY(run.check(weight_grad(dt, kvb, 2 * D, uz, D, NB, D, D, gr->w_k, true, s), "W_k gradient"));
-    RT_TRY(run.check(weight_grad(dt, qkvb + 2 * D * es, 3 * D, ux, D, NB, D, D, gr->w_v, false, s), "W_v gradient"));
-    RT_TRY(run.check(weight_grad(dt, kvb + D * es, 2 * D, uz, D, NB, D, D, gr->w_v, true, s), "W_v gradient"));
-    RT_TRY(run.check(weight_grad(dt, at(L.hbs), D, at(L.a), D, NB, D, D, gr->w_o, false, s), "W_o gradient"));
-    RT_TRY(run.check(weight_grad(dt, at(L.ubar), F, mm, D, NB, F, D, gr->w_1, false, s), "W_1 gradient"));
-    RT_TRY(run.check(weight_grad(dt, at(L.zbs), D, at(L.u), F, NB, D, F, gr->w_2, false, s), "W_2 gradient"));
+    // each a sum over all N*B rows of (adjoint of the product's output)^T (its input); the
+    // products sharing an input follow each other, which transposes that input once
+    const WgradScratch wsc{at(L.wta), at(L.wtu), f32(L.wpart), L.wrows};
+    auto wgrad = [&](const void* abar, int64_t lda, const void* u, int64_t ldu, int O, int I, float* out, bool acc,
+                     bool u_ready, const char* what) {
+        return run.check(weight_grad(dt, abar, lda, u, ldu, NB, O, I, out, acc, u_ready, wsc, s), what);
+    };
+    RT_TRY(wgrad(qkvb, 3 * D, ux, D, D, D, gr->w_q, false, false, "W_q gradient"));
+    RT_TRY(wgrad(qkvb + D * es, 3 * D, ux, D, D, D, gr->w_k, false, true, "W_k gradient"));
+    RT_TRY(wgrad(qkvb + 2 * D * es, 3 * D, ux, D, D, D, gr->w_v, false, true, "W_v gradient"));
+    RT_TRY(wgrad(kvb, 2 * D, uz, D, D, D, gr->w_k, true, false, "W_k gradient"));
+    RT_TRY(wgrad(kvb + D * es, 2 * D, uz, D, D, D, gr->w_v, true, true, "W_v gradient"));
+    RT_TRY(wgrad(at(L.hbs), D, at(L.a), D, D, D, gr->w_o, false, false, "W_o gradient"));
+    RT_TRY(wgrad(at(L.ubar), F, mm, D, F, D, gr->w_1, false, false, "W_1 gradient"));
+    RT_TRY(wgrad(at(L.zbs), D, at(L.u), F, D, F, gr->w_2, false, false, "W_2 gradient"));
     if (gr->g_attn) {
         RT_TRY(run.check(launch_gain_grad(dt, uxb, x, f32(L.rx), NB, D, f32(L.gpart), gr->g_attn, 0, s), "g_attn"));
         RT_TRY(run.check(launch_gain_grad(dt, f32(L.uzbar), z, f32(L.rz), NB, D, f32(L.gpart), gr->g_attn, 1, s),

@@ -214,7 +214,10 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
     const int qrow = wq0 + ql;
     const bool qvalid = qrow < nq;
     const int64_t j = (int64_t)q0 + min(qrow, nq - 1);
-    bf16x8 qop[4], aop[4];
+    // a_bar enters dP as two bf16 terms (the rounded value and its rounding
+    // error): dS = P (dP - delta) subtracts dP's weighted mean, so dP's relative
+    // rounding error would be amplified in dS
+    bf16x8 qop[4], aop[4], alo[4];
     {
         const bf16* qp = (const bf16*)b.q + j * slab + pair * DH + 8 * g;
         const float* ap = b.a_bar + j * slab + pair * DH + 8 * g;
@@ -223,8 +226,12 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
             qop[i] = *reinterpret_cast<const bf16x8*>(qp + 16 * i);
             const float4 x0 = *reinterpret_cast<const float4*>(ap + 16 * i);
             const float4 x1 = *reinterpret_cast<const float4*>(ap + 16 * i + 4);
-            aop[i][0] = (bf16)x0.x; aop[i][1] = (bf16)x0.y; aop[i][2] = (bf16)x0.z; aop[i][3] = (bf16)x0.w;
-            aop[i][4] = (bf16)x1.x; aop[i][5] = (bf16)x1.y; aop[i][6] = (bf16)x1.z; aop[i][7] = (bf16)x1.w;
+            const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                aop[i][e] = (bf16)xs[e];
+                alo[i][e] = (bf16)(xs[e] - (float)aop[i][e]);
+            }
         }
     }
     // a query past the block weighs 0: lse = +inf makes its probabilities 0
@@ -266,24 +273,39 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_q_mfma_kernel(BackwardArgs b, 
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[(c32 + krow) * STR + 16 * i + 8 * g]);
                 const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[(c32 + krow) * STR + 16 * i + 8 * g]);
                 st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[i], st, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, alo[i], dp, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, aop[i], dp, 0, 0, 0);
             }
-            bf16x8 s0, s1;  // dS^T in the B layout: keys 8g.. (e < 8) and 16+8g.. (e >= 8)
+            // dS^T in the B layout: keys 8g.. (e < 8) and 16+8g.. (e >= 8), as two bf16
+            // terms each (the rounded value and its rounding error): a query's score
+            // gradients sum to zero, so q_bar = sigma sum_i dS_i k_i cancels, and one
+            // bf16 rounding of dS would leave ~1e-2 relative error in it
+            bf16x8 s0, s1, r0, r1;
             // keys past a short block's end repeat its last row: their score gradients are zeroed
             const int live = rows - c32 - 8 * g;  // keys 8g + e (e < live) and 16 + 8g + e (e < live - 16) exist
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float pa = fast_exp2(__builtin_fmaf(st[e], sigma2, -lse));
                 const float pb = fast_exp2(__builtin_fmaf(st[e + 8], sigma2, -lse));
-                s0[e] = (bf16)(e < live ? pa * (dp[e] - dd) : 0.f);
-                s1[e] = (bf16)(e + 16 < live ? pb * (dp[e + 8] - dd) : 0.f);
+                const float da = e < live ? pa * (dp[e] - dd) : 0.f;
+                const float db = e + 16 < live ? pb * (dp[e + 8] - dd) : 0.f;
+                s0[e] = (bf16)da;
+                s1[e] = (bf16)db;
+                r0[e] = (bf16)(da - (float)s0[e]);
+                r1[e] = (bf16)(db - (float)s1[e]);
             }
-            const bf16* k_lo = &Kt[ql * STR + c32 + 8 * g];
-            const bf16* k_hi = &Kt[(32 + ql) * STR + c32 + 8 * g];
-            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k_lo), s0, d0, 0, 0, 0);
-            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k_lo + 16), s1, d0, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k_hi), s0, d1, 0, 0, 0);
-            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(k_hi + 16), s1, d1, 0, 0, 0);
+            const bf16x8 klo0 = *reinterpret_cast<const bf16x8*>(&Kt[ql * STR + c32 + 8 * g]);
+            const bf16x8 klo1 = *reinterpret_cast<const bf16x8*>(&Kt[ql * STR + c32 + 8 * g + 16]);
+            const bf16x8 khi0 = *reinterpret_cast<const bf16x8*>(&Kt[(32 + ql) * STR + c32 + 8 * g]);
+            const bf16x8 khi1 = *reinterpret_cast<const bf16x8*>(&Kt[(32 + ql) * STR + c32 + 8 * g + 16]);
+            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo0, r0, d0, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo1, r1, d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi0, r0, d1, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi1, r1, d1, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo0, s0, d0, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo1, s1, d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi0, s0, d1, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi1, s1, d1, 0, 0, 0);
         }
     }
     if (!qvalid) return;
@@ -315,6 +337,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
     constexpr int DH = 64, QT = 64, STR = 72, NT = 64 * WAVES;
     __shared__ __attribute__((aligned(16))) bf16 Qs[QT * STR];
     __shared__ __attribute__((aligned(16))) bf16 As[QT * STR];
+    __shared__ __attribute__((aligned(16))) bf16 Al[QT * STR];  // a_bar's rounding error (dP, as on the query side)
     __shared__ __attribute__((aligned(16))) bf16 Qt[DH * STR];
     __shared__ __attribute__((aligned(16))) bf16 At[DH * STR];
     __shared__ __attribute__((aligned(16))) float Ls[QT];
@@ -360,11 +383,16 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
             const bf16x8 qx = *reinterpret_cast<const bf16x8*>(qb + (int64_t)(qt0 + r) * slab + ch);
             const float4 a0 = *reinterpret_cast<const float4*>(ab + (int64_t)(qt0 + r) * slab + ch);
             const float4 a1 = *reinterpret_cast<const float4*>(ab + (int64_t)(qt0 + r) * slab + ch + 4);
-            bf16x8 ax;
-            ax[0] = (bf16)a0.x; ax[1] = (bf16)a0.y; ax[2] = (bf16)a0.z; ax[3] = (bf16)a0.w;
-            ax[4] = (bf16)a1.x; ax[5] = (bf16)a1.y; ax[6] = (bf16)a1.z; ax[7] = (bf16)a1.w;
+            const float as_[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            bf16x8 ax, al;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ax[e] = (bf16)as_[e];
+                al[e] = (bf16)(as_[e] - (float)ax[e]);
+            }
             *reinterpret_cast<bf16x8*>(&Qs[(c >> 3) * STR + ch]) = qx;
             *reinterpret_cast<bf16x8*>(&As[(c >> 3) * STR + ch]) = ax;
+            *reinterpret_cast<bf16x8*>(&Al[(c >> 3) * STR + ch]) = al;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 Qt[(ch + e) * STR + (c >> 3)] = qx[e];
@@ -390,7 +418,9 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
             for (int i = 0; i < 4; ++i) {
                 const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[(c32 + arow) * STR + 16 * i + 8 * g]);
                 const bf16x8 aa = *reinterpret_cast<const bf16x8*>(&As[(c32 + arow) * STR + 16 * i + 8 * g]);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[(c32 + arow) * STR + 16 * i + 8 * g]);
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[i], sc, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, vop[i], dp, 0, 0, 0);
                 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aa, vop[i], dp, 0, 0, 0);
             }
             // element e holds query c32 + (e&7) + 8g + 16(e>>3)
@@ -406,15 +436,20 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
                                   l2.x, l2.y, l2.z, l2.w, l3.x, l3.y, l3.z, l3.w};
             const float dv[16] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w,
                                   e2.x, e2.y, e2.z, e2.w, e3.x, e3.y, e3.z, e3.w};
-            bf16x8 p0, p1, s0, s1;
+            // dS as two bf16 terms each (the rounded value and its rounding error), as
+            // in the query side
+            bf16x8 p0, p1, s0, s1, r0, r1;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float pa = fast_exp2(__builtin_fmaf(sc[e], sigma2, -lv[e]));
                 const float pb = fast_exp2(__builtin_fmaf(sc[e + 8], sigma2, -lv[e + 8]));
                 p0[e] = (bf16)pa;
                 p1[e] = (bf16)pb;
-                s0[e] = (bf16)(pa * (dp[e] - dv[e]));
-                s1[e] = (bf16)(pb * (dp[e + 8] - dv[e + 8]));
+                const float da = pa * (dp[e] - dv[e]), db = pb * (dp[e + 8] - dv[e + 8]);
+                s0[e] = (bf16)da;
+                s1[e] = (bf16)db;
+                r0[e] = (bf16)(da - (float)s0[e]);
+                r1[e] = (bf16)(db - (float)s1[e]);
             }
             const bf16* a_lo = &At[kl * STR + c32 + 8 * g];
             const bf16* a_hi = &At[(32 + kl) * STR + c32 + 8 * g];
@@ -424,6 +459,10 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kv_mfma_kernel(BackwardArgs b,
             dv0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a_lo + 16), p1, dv0, 0, 0, 0);
             dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a_hi), p0, dv1, 0, 0, 0);
             dv1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a_hi + 16), p1, dv1, 0, 0, 0);
+            dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_lo), r0, dk0, 0, 0, 0);
+            dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_lo + 16), r1, dk0, 0, 0, 0);
+            dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_hi), r0, dk1, 0, 0, 0);
+            dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_hi + 16), r1, dk1, 0, 0, 0);
             dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_lo), s0, dk0, 0, 0, 0);
             dk0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_lo + 16), s1, dk0, 0, 0, 0);
             dk1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(q_hi), s0, dk1, 0, 0, 0);

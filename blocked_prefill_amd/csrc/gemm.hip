@@ -204,7 +204,8 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
     constexpr int HB = BN / 2;
     const int seg = PAIRED ? 0 : n0 / g.seg_n;
     const int pcol = (n0 / BN) * HB;  // PAIRED: first column of this tile in each segment
-    const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * g.K;
+    const int64_t ldw = g.ldw ? g.ldw : g.K;  // row stride of W
+    const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * ldw;
     const bf16* A = (const bf16*)g.A;
 
     // this thread's chunks: slot s = NTG*i + gtid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
@@ -222,14 +223,16 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int s = NTG * i + gtid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-        w_src[i] = PAIRED ? (const bf16*)g.W[r >= HB] + (int64_t)(pcol + r % HB) * g.K + c * 8
-                          : W + (int64_t)r * g.K + c * 8;
+        w_src[i] = PAIRED ? (const bf16*)g.W[r >= HB] + (int64_t)(pcol + r % HB) * ldw + c * 8
+                          : W + (int64_t)r * ldw + c * 8;
     }
 
     bf16x8 ra[D][LA], rw[D][LW];
+    const int a_k = g.a_k ? g.a_k : g.K;  // A's own columns: column k reads k mod a_k (split weights)
     auto load = [&](int u, int k0) {
+        const int ka = k0 >= a_k ? k0 - a_k : k0;
 #pragma unroll
-        for (int i = 0; i < LA; ++i) ra[u][i] = *reinterpret_cast<const bf16x8*>(a_src[i] + k0);
+        for (int i = 0; i < LA; ++i) ra[u][i] = *reinterpret_cast<const bf16x8*>(a_src[i] + ka);
 #pragma unroll
         for (int i = 0; i < LW; ++i) rw[u][i] = *reinterpret_cast<const bf16x8*>(w_src[i] + k0);
     };
@@ -379,7 +382,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
         for (int r = tid; r < BM; r += NT) {
             float v = 0.f;
             for (int q = 0; q < qpr; ++q) v += qsum[r * 16 + q];
-            rs[r] = rsqrtf(v / (float)g.K + g.eps);
+            rs[r] = g.no_rms ? 1.f : rsqrtf(v / (float)a_k + g.eps);
         }
     }
     if (FLAGS & EPI_RMS) {
@@ -389,7 +392,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
                 float s2 = ss[i];
 #pragma unroll
                 for (int x = MF; x < 64; x <<= 1) s2 += __shfl_xor(s2, x, 64);  // lanes sharing the row
-                if (lgrp == 0) rs[wm * TMW + i * MF + lrow] = rsqrtf(s2 / (float)g.K + g.eps);
+                if (lgrp == 0) rs[wm * TMW + i * MF + lrow] = g.no_rms ? 1.f : rsqrtf(s2 / (float)g.K + g.eps);
             }
         }
     }
@@ -580,13 +583,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
     const int col = (int)(idx % g.N);
     const int seg = col / g.seg_n;
     const float* a = (const float*)g.A + row * g.lda;
-    const float* w = (const float*)g.W[seg] + (int64_t)(col % g.seg_n) * g.K;
+    const float* w = (const float*)g.W[seg] + (int64_t)(col % g.seg_n) * (g.ldw ? g.ldw : g.K);
     float acc = 0.f, ss = 0.f;
     for (int k = 0; k < g.K; ++k) {
         acc += a[k] * w[k];
         if (FLAGS & EPI_RMS) ss += a[k] * a[k];
     }
-    const float rstd = (FLAGS & EPI_RMS) ? rsqrtf(ss / (float)g.K + g.eps) : 1.f;
+    const float rstd = ((FLAGS & EPI_RMS) && !g.no_rms) ? rsqrtf(ss / (float)g.K + g.eps) : 1.f;
     epilogue_store<FLAGS, TR, float>(g, (float*)g.C[seg], row, col, acc, rstd);
 }
 
@@ -733,6 +736,9 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(gs, s);
             break;
+        case GemmKind::WGRAD:  // K of 10^4..10^6 rows per product: 128x128 tiles, eight waves of 32x64
+            if constexpr (KS == 1) return run_pipe<float, float, 0, 128, 128, 4, 2, 2, 32>(gs, s);
+            break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
                 if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(gs, s);
@@ -804,6 +810,7 @@ static hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t 
         case GemmKind::W1_PRE: e = run_f32<float, EPI_RMS>(g, s); break;
         case GemmKind::PLAIN: e = run_f32<float, 0>(g, s); break;
         case GemmKind::W2_BWD: e = run_f32<float, EPI_DGELU>(g, s); break;
+        case GemmKind::WGRAD: e = run_f32<float, 0>(g, s); break;
     }
     if (e != hipSuccess || !g.qkn_mask) return e;
     return qk_norm_f32(g, s);
@@ -811,7 +818,8 @@ static hipError_t launch_gemm_f32(GemmKind kind, const GemmArgs& g, hipStream_t 
 
 // Products that may share a launch: the same shape and the same epilogue inputs.
 static bool same_shape(const GemmArgs& a, const GemmArgs& b) {
-    return a.N == b.N && a.K == b.K && a.seg_n == b.seg_n && a.n_parts == b.n_parts &&
+    return a.N == b.N && a.K == b.K && a.a_k == b.a_k && a.ldw == b.ldw && a.no_rms == b.no_rms && a.seg_n == b.seg_n &&
+           a.n_parts == b.n_parts &&
            (a.rss_in != nullptr) == (b.rss_in != nullptr) && a.qkn_mask == b.qkn_mask &&
            a.head_dim == b.head_dim && a.M > 0 && b.M > 0;
 }
@@ -890,11 +898,25 @@ hipError_t launch_row_sumsq(rt_dtype dt, const void* x, int64_t rows, int D, flo
 
 // ---------------------------------------------------------------- gain folding
 
-template <typename T>
-__global__ __launch_bounds__(256) void fold_gain_kernel(const T* W, const float* g, T* out, int64_t rows, int cols) {
+__global__ __launch_bounds__(256) void fold_gain_f32_kernel(const float* W, const float* g, float* out, int64_t rows,
+                                                             int cols) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= rows * cols) return;
-    out[idx] = from_f32<T>(to_f32(W[idx]) * g[idx % cols]);
+    out[idx] = W[idx] * g[idx % cols];
+}
+
+// bf16: the product W g (exact in fp32 up to one rounding) as a rounded bf16
+// value and the bf16 of what that rounding dropped, in the two halves of the row.
+__global__ __launch_bounds__(256) void fold_gain_bf16_kernel(const bf16* W, const float* g, bf16* out, int64_t rows,
+                                                             int cols) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * cols) return;
+    const int64_t r = idx / cols;
+    const int c = (int)(idx % cols);
+    const float p = (float)W[idx] * g[c];
+    const bf16 hi = (bf16)p;
+    out[r * 2 * cols + c] = hi;
+    out[r * 2 * cols + cols + c] = (bf16)(p - (float)hi);
 }
 
 hipError_t launch_fold_gain(rt_dtype dt, const void* W, const float* g, void* W_out, int64_t rows, int cols,
@@ -902,10 +924,9 @@ hipError_t launch_fold_gain(rt_dtype dt, const void* W, const float* g, void* W_
     const int64_t n = rows * cols;
     const dim3 grid((uint32_t)((n + 255) / 256));
     if (dt == RT_BF16)
-        hipLaunchKernelGGL(fold_gain_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)W, g, (bf16*)W_out, rows, cols);
+        hipLaunchKernelGGL(fold_gain_bf16_kernel, grid, dim3(256), 0, s, (const bf16*)W, g, (bf16*)W_out, rows, cols);
     else
-        hipLaunchKernelGGL(fold_gain_kernel<float>, grid, dim3(256), 0, s, (const float*)W, g, (float*)W_out, rows,
-                           cols);
+        hipLaunchKernelGGL(fold_gain_f32_kernel, grid, dim3(256), 0, s, (const float*)W, g, (float*)W_out, rows, cols);
     return hipGetLastError();
 }
 

@@ -12,10 +12,6 @@
 //   x_bar = g y_bar / r - x sum(g y_bar x) / (d r^3),   g_bar += y_bar x / r.
 // The GELU's derivative Phi(u) + u phi(u) is applied in the W_2^T product's
 // epilogue (gemm.hip).
-#include <rocblas/rocblas.h>
-
-#include <mutex>
-
 #include "rt_device.h"
 #include "rt_internal.h"
 
@@ -307,38 +303,115 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 
 // ------------------------------------------------------------- weight gradients
 //
-// W_bar[o][i] (+)= sum_r A_bar[r][o] U[r][i] over R rows (a plain GEMM with the
-// reduction over positions x batch rows), on rocBLAS: in column-major terms
-// W_bar^T (I x O) = U^T (I x R) * A_bar (R x O).
+// W_bar[o][i] (+)= sum_r A_bar[r][o] U[r][i] over R = N*B rows. The reduction
+// runs along the rows of both operands, so both are transposed first into
+// row-major [O][Rp] and [I][Rp] copies (zero past row R, Rp a multiple of the
+// split), and the product C = A_bar^T U^T^T is the library's MFMA GEMM with
+// K = Rp, split into up to kWgradSplits K ranges run as one grouped launch
+// (at O = I = 1024 a single product has 64 output tiles; eight K ranges give
+// 512 workgroups), each writing its own fp32 partial; a last pass adds the
+// partials (and the previous gradient when accumulating) in a fixed order.
 
 namespace {
-// One handle per device, created on first use and kept until the process
-// ends. A handle's stream is state: the lock keeps each call's set-stream and
-// product together when several threads enqueue on one device.
-rocblas_handle g_blas[64];
-std::mutex g_blas_lock[64];
+
+// dst[c][r] = r < rows ? src[r * lds + c] : 0 for c < cols, r < rows_pad
+// (64x64 tiles through LDS; a thread moves 4 consecutive elements each way).
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const T* src, int64_t rows, int64_t lds, int cols,
+                                                            T* dst, int64_t rows_pad) {
+    __shared__ T tile[64][64 + 4];
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int c0 = blockIdx.x * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int q = tid + 256 * it, rl = q >> 4, cl = (q & 15) * 4;  // row, first column of the quad
+        const int64_t r = r0 + rl;
+        const int c = c0 + cl;
+        T v[4] = {T(0.f), T(0.f), T(0.f), T(0.f)};
+        if (r < rows && c < cols) {  // cols % 4 == 0: a quad is all in or all out
+            const T* p = src + r * lds + c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = p[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[rl][cl + e] = v[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int q = tid + 256 * it, cl = q >> 4, rl = (q & 15) * 4;  // destination row (column of src), 4 rows
+        const int c = c0 + cl;
+        if (c >= cols) continue;
+        T* p = dst + (int64_t)c * rows_pad + r0 + rl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = tile[rl + e][cl];
+    }
+}
+
+// out[i] = (accumulate ? out[i] : 0) + sum_s part[s][i], s in order (n % 4 == 0).
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* part, int splits, int64_t n, float* out,
+                                                           int accumulate) {
+    for (int64_t q = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; q < n; q += (int64_t)gridDim.x * 256 * 4) {
+        float4 acc = accumulate ? *reinterpret_cast<const float4*>(out + q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < splits; ++sp) {
+            const float4 v = *reinterpret_cast<const float4*>(part + sp * n + q);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
+        *reinterpret_cast<float4*>(out + q) = acc;
+    }
+}
+
+template <typename T>
+hipError_t transpose_pad(const void* src, int64_t rows, int64_t lds, int cols, void* dst, int64_t rows_pad,
+                         hipStream_t s) {
+    if (cols % 4 || rows_pad % 64 || rows_pad / 64 > 65535) return hipErrorInvalidValue;
+    const dim3 grid((uint32_t)((cols + 63) / 64), (uint32_t)(rows_pad / 64));
+    hipLaunchKernelGGL(transpose_pad_kernel<T>, grid, dim3(256), 0, s, (const T*)src, rows, lds, cols, (T*)dst,
+                       rows_pad);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+WgradPlan wgrad_plan(int64_t rows) {
+    WgradPlan p{};
+    p.splits = rows >= (int64_t)kWgradSplits * 1024 ? kWgradSplits : 1;
+    const int64_t unit = 128 * (int64_t)p.splits;  // every split's K an even number of 64-wide tiles
+    p.rows_pad = (rows + unit - 1) / unit * unit;
+    return p;
 }
 
 hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u, int64_t ldu, int64_t R, int O,
-                       int I, float* out, bool accumulate, hipStream_t s) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+                       int I, float* out, bool accumulate, bool u_ready, const WgradScratch& ws, hipStream_t s) {
+    const WgradPlan pl = wgrad_plan(R);
+    if (pl.rows_pad != ws.rows_pad || O % 4 || I % 4) return hipErrorInvalidValue;
+    hipError_t e = dt == RT_BF16 ? transpose_pad<bf16>(abar, R, lda, O, ws.ta, pl.rows_pad, s)
+                                 : transpose_pad<float>(abar, R, lda, O, ws.ta, pl.rows_pad, s);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (R > 0x7fffffffLL || lda > 0x7fffffffLL || ldu > 0x7fffffffLL) return hipErrorInvalidValue;
-    std::lock_guard<std::mutex> hold(g_blas_lock[dev]);
-    if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-        g_blas[dev] = nullptr;
-        return hipErrorUnknown;
+    if (!u_ready) {  // U^T is already in ws.tu from the previous call with the same U
+        e = dt == RT_BF16 ? transpose_pad<bf16>(u, R, ldu, I, ws.tu, pl.rows_pad, s)
+                          : transpose_pad<float>(u, R, ldu, I, ws.tu, pl.rows_pad, s);
+        if (e != hipSuccess) return e;
     }
-    if (rocblas_set_stream(g_blas[dev], s) != rocblas_status_success) return hipErrorUnknown;
-    const float alpha = 1.f, beta = accumulate ? 1.f : 0.f;
-    const rocblas_datatype ab = dt == RT_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const rocblas_status st =
-        rocblas_gemm_ex(g_blas[dev], rocblas_operation_none, rocblas_operation_transpose, I, O, (rocblas_int)R, &alpha,
-                        u, ab, (rocblas_int)ldu, abar, ab, (rocblas_int)lda, &beta, out, rocblas_datatype_f32_r, I,
-                        out, rocblas_datatype_f32_r, I, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-    return st == rocblas_status_success ? hipSuccess : hipErrorUnknown;
+    const size_t es = dt == RT_BF16 ? 2 : 4;
+    const int64_t kc = pl.rows_pad / pl.splits;
+    GemmArgs g[kWgradSplits];
+    for (int sp = 0; sp < pl.splits; ++sp) {
+        GemmArgs& a = g[sp];
+        a = GemmArgs{};
+        a.A = (const char*)ws.ta + sp * kc * es; a.lda = pl.rows_pad;
+        a.W[0] = (const char*)ws.tu + sp * kc * es; a.ldw = pl.rows_pad;
+        a.C[0] = ws.part + (int64_t)sp * O * I; a.ldc = I; a.seg_n = I;
+        a.M = O; a.N = I; a.K = (int32_t)kc;
+    }
+    e = launch_gemm_group(dt, GemmKind::WGRAD, g, pl.splits, s);
+    if (e != hipSuccess) return e;
+    const int64_t n = (int64_t)O * I;
+    const int64_t blocks = (n / 4 + 255) / 256;
+    hipLaunchKernelGGL(wgrad_reduce_kernel, dim3((uint32_t)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, s,
+                       ws.part, pl.splits, n, out, accumulate ? 1 : 0);
+    return hipGetLastError();
 }
 
 }  // namespace rt

@@ -104,6 +104,14 @@ struct GemmArgs {
     float eps;
     int64_t M;
     int32_t N, K;
+    // Columns of A (0: K). When a_k < K, column k of the product reads column
+    // k mod a_k of A: a bf16 weight whose RMS gain is folded in is stored as
+    // two bf16 halves side by side ([rows][2 a_k]: the rounded product, then
+    // its rounding error), and both halves multiply the same A row. The RMS
+    // of an A row is taken over a_k columns.
+    int32_t a_k;
+    int64_t ldw;          // row stride of W (0: K)
+    int32_t no_rms;       // 1: EPI_RMS / EPI_RMS_PARTS scale rows by 1 (a persistent pair read from z itself)
     const float* rss_in;  // [M][n_parts] (EPI_RMS_PARTS), n_parts % 4 == 0, <= 64
     int32_t n_parts;
     float* rss_out;       // [M][N / tile width] (EPI_ROWSS)
@@ -127,6 +135,7 @@ enum class GemmKind {
     W1_PRE,   // A = h (bf16 copy with RMS partials, or fp32), RMS, C = W_1 RMS(h) before the GELU (T)
     PLAIN,    // C (fp32) = A (T) * W^T, no epilogue (the backward's adjoint products)
     W2_BWD,   // C (T) = (A * W^T) * GELU'(R), R = the MLP's pre-activation (T); per-position rows only
+    WGRAD,    // C (fp32) = A * W^T with a long K (a weight gradient's reduction over rows; W row stride ldw)
 };
 hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_t s);
 // n products of one kind and shape (the same N, K and epilogue inputs; row
@@ -162,12 +171,30 @@ int64_t gain_grad_blocks(int64_t rows);
 hipError_t launch_gain_grad(rt_dtype x_dt, const float* ybar, const void* x, const float* rinv, int64_t rows, int D,
                             float* part, float* out, int accumulate, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
-// out[o][i] (+)= sum_r abar[r][o] u[r][i] (abar row stride lda, u row stride ldu, both in dt; out fp32 [O][I]).
+// Weight gradients out[o][i] (+)= sum_r abar[r][o] u[r][i] over R rows (abar row stride lda, u row stride ldu,
+// both in dt; out fp32 [O][I]; O, I multiples of 4, of 128 for bf16): both operands transposed into ws
+// (ta [O][rows_pad], tu [I][rows_pad]), the product split into `splits` K ranges (fp32 partials in ws.part,
+// splits * O * I floats), then added up. u_ready: ws.tu already holds this u (the previous call's).
+constexpr int kWgradSplits = 8;
+struct WgradPlan {
+    int64_t rows_pad;  // R rounded up to 128 * splits
+    int splits;
+};
+WgradPlan wgrad_plan(int64_t rows);
+struct WgradScratch {
+    void* ta;          // [max O][rows_pad] (dt)
+    void* tu;          // [max I][rows_pad] (dt)
+    float* part;       // [splits][max O*I]
+    int64_t rows_pad;
+};
 hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u, int64_t ldu, int64_t R, int O,
-                       int I, float* out, bool accumulate, hipStream_t s);
+                       int I, float* out, bool accumulate, bool u_ready, const WgradScratch& ws, hipStream_t s);
 bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K);
 
-// W_out[r][c] = W[r][c] * g[c] (fold an RMS gain into the following projection).
+// Fold an RMS gain into the following projection, p[r][c] = W[r][c] * g[c]
+// computed in fp32: fp32 layers store W_out = p ([rows][cols]); bf16 layers
+// store W_out = [bf16(p) | bf16(p - bf16(p))] ([rows][2 cols]), whose sum is
+// p to ~2^-17 relative (read with a_k = cols, K = 2 cols).
 hipError_t launch_fold_gain(rt_dtype dt, const void* W, const float* g, void* W_out, int64_t rows, int cols,
                             hipStream_t s);
 

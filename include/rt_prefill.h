@@ -34,9 +34,9 @@
  *     the calling thread's last error.
  *   - The library allocates no device memory in any entry point except
  *     plan creation (rt_layer_plan_create, rt_stack_plan_create: a plan owns
- *     only its captured HIP graphs) and the first rt_layer_backward call on a
- *     device, which creates that device's rocBLAS handle (rocBLAS's own device
- *     workspace, kept until the process ends).
+ *     only its captured HIP graphs). Every product, the weight gradients
+ *     included, runs in the library's own kernels: it calls no vendor GEMM
+ *     library.
  */
 #ifndef RT_PREFILL_H
 #define RT_PREFILL_H
@@ -91,11 +91,19 @@ typedef struct {
 /* Layer shape. d_model must equal n_heads*head_dim. rms_eps is the epsilon
  * of both RMS normalisations, RMS(v) = g * v / sqrt(mean(v^2) + eps).
  * residual_scale rho multiplies both residual branches (the pages use
- * 1/sqrt(number of layers); 1.0 gives the plain pre-LN layer). */
+ * 1/sqrt(number of layers); 1.0 gives the plain pre-LN layer).
+ * kv_source_norm (0 or 1) chooses how an RT layer forms its persistent pair
+ * from the output z_t (translated paper section 2.2, whose text breaks off
+ * before this formula): 1 (the reading the workloads use) applies the same
+ * map as the ephemeral pair, k_t = W_k RMS_attn(z_t), v_t = W_v RMS_attn(z_t);
+ * 0 takes the formula literally, k_t = W_k z_t, v_t = W_v z_t (no RMS, no
+ * g_attn). The Transformer layer (RT_FLAG_TRANSFORMER) needs 1: its pair is
+ * its ephemeral pair. */
 typedef struct {
     rt_attn_desc attn;
     int32_t d_model, d_ff;
     float rms_eps, residual_scale;
+    int32_t kv_source_norm;
     uint32_t flags;
 } rt_layer_desc;
 
@@ -105,7 +113,11 @@ typedef struct {
  * g_attn (RMS gain before Q/K/V) and g_mlp (RMS gain before the MLP) are
  * fp32 [d], or NULL for a vector of ones; so are g_q and g_k, the query/key
  * norm gains (read only with RT_FLAG_QK_NORM; head h uses entries
- * h*head_dim .. h*head_dim+head_dim-1). */
+ * h*head_dim .. h*head_dim+head_dim-1). A given g_attn or g_mlp is folded
+ * into the projection it feeds, W[r][c] g[c], in fp32 (bf16 layers keep the
+ * folded weight as two bf16 terms, the rounded product and its rounding
+ * error, so the fold adds no bf16 rounding; those products then run over 2d
+ * columns). */
 typedef struct {
     const void *w_q, *w_k, *w_v, *w_o, *w_1, *w_2;
     const float *g_attn, *g_mlp;

@@ -26,7 +26,15 @@ and the remark that it can be batched outside the position loop (section
     of an outer product (adjoint of a product's output times its input).
 RMS(x) = g x / r with r = sqrt(mean(x^2) + eps) has the adjoint
     x_bar = g y_bar / r - x sum(g y_bar x) / (d r^3),  g_bar = sum(y_bar x / r).
-No bf16 rounding is modelled: this is the gradient of the exact layer.
+With round_bf16 unset this is the gradient of the exact layer. With it set,
+the derivatives are taken at the forward values a bf16 layer holds between
+its kernels (rt_oracle.c's bf16 mode): q, k', v', the persistent k, v, the
+attention output a and the output z as stored (rounded to bf16, RNE); the
+MLP's pre-activation u = W_1 (g_mlp * bf16(h)) / rms(h) and its activation
+GELU(u) as stored; and the normalised inputs of the weight products,
+RMS_attn(x), RMS_attn(bf16(z)) and RMS_mlp(h), as stored. h stays exact
+(a bf16 layer keeps it in fp32). The roundings themselves are taken as the
+identity (they have no derivative), and the adjoints stay exact.
 Plain numpy, loops over positions; the forward values come from rt_oracle.c.
 """
 from __future__ import annotations
@@ -63,12 +71,17 @@ def _gelu_grad(u):
 
 
 def layer_backward(x, weights: dict, z_bar, *, n_heads: int, softmax_scale: float, residual_scale: float = 1.0,
-                   rms_eps: float = 1e-6) -> dict:
-    """Gradients of L = sum(z_bar * z) for the RT layer on x [N][R][d] (naive schedule, no rounding).
+                   rms_eps: float = 1e-6, round_bf16: bool = False) -> dict:
+    """Gradients of L = sum(z_bar * z) for the RT layer on x [N][R][d] (naive schedule).
 
-    Returns float64 arrays by name: x, w_q, w_k, w_v, w_o, w_1, w_2, g_attn, g_mlp.
+    round_bf16: the derivatives are taken at the forward values as a bf16 layer stores them.
+    Returns float64 arrays by name: x, w_q, w_k, w_v, w_o, w_1, w_2, g_attn, g_mlp; with
+    round_bf16 also "z_stored", the forward output as stored (float32, bf16 values).
     """
     from . import layer_forward  # the forward values (rt_oracle.c, IEEE double)
+    from . import round_bf16 as _round
+
+    keep = (lambda t: _round(t)) if round_bf16 else (lambda t: t)
 
     x = np.asarray(x, dtype=np.float32)
     N, R, d = x.shape
@@ -81,16 +94,23 @@ def layer_backward(x, weights: dict, z_bar, *, n_heads: int, softmax_scale: floa
     rho, sigma, eps = residual_scale, softmax_scale, rms_eps
 
     fw = layer_forward(x, weights, n_heads=H, softmax_scale=sigma, residual_scale=rho, rms_eps=rms_eps,
-                       want=("z", "k", "v", "q", "k_eph", "v_eph", "a", "h"))
+                       round_bf16=round_bf16, want=("z", "k", "v", "q", "k_eph", "v_eph", "a", "h"))
     xd = x.astype(np.float64)
-    z, h, a = fw["z"], fw["h"], fw["a"]
+    z = fw["x_next"].astype(np.float64) if round_bf16 else fw["z"]   # the output as stored
+    h, a = fw["h"], keep(fw["a"])
     heads = lambda t: t.reshape(N, R, H, dh)
-    q, ke, ve, k, v = (heads(fw[n]) for n in ("q", "k_eph", "v_eph", "k", "v"))
+    q, ke, ve, k, v = (heads(keep(fw[n])) for n in ("q", "k_eph", "v_eph", "k", "v"))
     a_h = heads(a)
-    m, _ = _rms_fwd(h, g_mlp, eps)
-    u = m @ W["w_1"].T                                  # [N][R][F], pre-activation
+    m, rh = _rms_fwd(h, g_mlp, eps)
+    if round_bf16:
+        u = keep((g_mlp * keep(h) * rh) @ W["w_1"].T)   # the product reads h as bf16, its rms exact
+        m = keep(m)
+    else:
+        u = m @ W["w_1"].T                              # [N][R][F], pre-activation
     ux, _ = _rms_fwd(xd, g_attn, eps)
     uz, _ = _rms_fwd(z, g_attn, eps)
+    ux, uz = keep(ux), keep(uz)
+    gelu_u = keep(_gelu(u))
 
     zb = np.asarray(z_bar, dtype=np.float64)
     k_bar = np.zeros((N, R, H, dh))
@@ -139,14 +159,17 @@ def layer_backward(x, weights: dict, z_bar, *, n_heads: int, softmax_scale: floa
     dx, dg = _rms_bwd(xd, g_attn, ux_bar, eps)
     g_attn_bar += dg
     outer = lambda A, B: np.einsum("nro,nri->oi", A, B)
-    return {
+    out = {
         "x": h_bar + dx,
         "w_q": outer(flat(q_bar), ux),
         "w_k": outer(flat(ke_bar), ux) + outer(flat(k_bar), uz),
         "w_v": outer(flat(ve_bar), ux) + outer(flat(v_bar), uz),
         "w_o": rho * outer(h_bar, a),
         "w_1": outer(u_bar, m),
-        "w_2": rho * outer(zt_bar, _gelu(u)),
+        "w_2": rho * outer(zt_bar, gelu_u),
         "g_attn": g_attn_bar,
         "g_mlp": g_mlp_bar,
     }
+    if round_bf16:
+        out["z_stored"] = fw["x_next"]
+    return out

@@ -1,13 +1,23 @@
 """Helpers of the GPU parity tests: device tensors, the library's entry points
 driven over whole sequences, and the parity bars.
 
-Bars (fp32: relative L2 <= 1e-5; bf16: max |gpu - ref| <= 2e-2 and relative
-L2 <= 5e-3) compare each tensor the GPU stores in bf16 with the oracle's value
-of that tensor before its own rounding; the oracle rounds to bf16 where the
-library holds bf16 between steps. A bf16 output cannot be closer to the exact
-value than half its own unit in the last place (0.031 for |value| in [8, 16)),
-so the bf16 max-abs bar applies to the error beyond that half-ulp; the raw
-maximum is reported alongside.
+Bars. fp32: relative L2 <= 1e-5. bf16: relative L2 <= 5e-3 and max-abs 2e-2,
+each tensor the GPU stores in bf16 against the oracle's value of that tensor
+before its own rounding (the oracle rounds to bf16 exactly where the library
+holds bf16 between kernels). The max-abs bar is raw (|gpu - ref| <= 2e-2)
+for elements with |ref| < 4; at |ref| >= 4 a bf16 output's own rounding is
+already up to 0.0156 (0.031 from 8), so those elements are held to half
+their ulp + the bar, and counted in the report.
+
+Where the layer's recurrence is long (tens of positions or more), a bf16
+layer turns rounding decisions that differ at the 1e-8 level into
+differences of 0.02-0.03 (the persistent pairs feed every later position):
+the oracle against itself with its weights perturbed by 1e-7 relative (the
+level of fp32 rounding) already misses a raw 2e-2 there. Those tests measure
+that noise floor in the same test (oracle_with_floor: the oracle run again on
+perturbed weights; data still flows from the oracle only) and hold the GPU to
+max(2e-2, FLOOR_MARGIN x the floor): a GPU result within the bar deviates
+from the oracle no more than the oracle deviates from itself.
 """
 import math
 import os
@@ -22,6 +32,9 @@ if ROOT not in sys.path:
 import blocked_prefill_amd as rt  # noqa: E402
 
 TOL = {"f32": {"rel_l2": 1e-5}, "bf16": {"rel_l2": 5e-3, "max_abs": 2e-2}}
+BIG = 4.0  # |ref| from which a bf16 element is held to half its ulp + max_abs
+PERTURB = 1e-7      # relative perturbation of every weight for the oracle's noise floor
+FLOOR_MARGIN = 1.5  # the GPU's max-abs may reach this multiple of the oracle's own floor
 
 
 def ensure_built():
@@ -50,26 +63,61 @@ def host(t) -> np.ndarray:
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 
 
-def parity(gpu, ref, dt: str, what: str = ""):
-    """Return the metrics; raise AssertionError with them when the bar is missed."""
+def parity(gpu, ref, dt: str, what: str = "", floor=None, stored=False):
+    """Return the metrics; raise AssertionError with them when the bar is missed.
+
+    floor: the oracle's own max-abs noise floor for this tensor (oracle_with_floor);
+    the bf16 max-abs bar is then max(2e-2, FLOOR_MARGIN * floor).
+    stored: ref is itself a bf16 result (another GPU path), not a value before its
+    rounding; the two may then also sit one rounding decision apart (one ulp)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{what}: non-finite GPU values"
     err = gpu - ref
     rel = float(np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-300))
-    mx = float(np.max(np.abs(err))) if err.size else 0.0
+    ae = np.abs(err)
+    mx = float(ae.max()) if err.size else 0.0
     m = {"rel_l2": rel, "max_abs": mx}
-    bar = TOL[dt]
+    bar = dict(TOL[dt])
+    if floor is not None and dt == "bf16":
+        bar["max_abs"] = max(bar["max_abs"], FLOOR_MARGIN * float(floor))
+        m["oracle_floor"] = float(floor)
     ok = rel <= bar["rel_l2"]
-    if dt == "bf16" and err.size:
-        excess = np.abs(err) - 0.5 * bf16_ulp(ref)
-        i = int(np.argmax(excess))
-        m["max_abs_beyond_half_ulp"] = float(excess.flat[i])
-        m["at_ref"] = float(ref.flat[i])
-        ok = ok and m["max_abs_beyond_half_ulp"] <= bar["max_abs"]
+    if dt == "bf16" and err.size and stored:
+        m["beyond_one_ulp"] = float((ae - bf16_ulp(np.maximum(np.abs(ref), np.abs(gpu)))).max())
+        ok = ok and m["beyond_one_ulp"] <= bar["max_abs"]
+    elif dt == "bf16" and err.size:
+        big = np.abs(ref) >= BIG
+        m["max_abs_below_4"] = float(ae[~big].max()) if (~big).any() else 0.0
+        m["n_at_or_above_4"] = int(big.sum())
+        ok = ok and m["max_abs_below_4"] <= bar["max_abs"]
+        if big.any():
+            m["max_abs_at_or_above_4"] = float(ae[big].max())
+            m["beyond_half_ulp_at_or_above_4"] = float((ae[big] - 0.5 * bf16_ulp(ref[big])).max())
+            ok = ok and m["beyond_half_ulp_at_or_above_4"] <= bar["max_abs"]
     assert ok, f"{what}: {m} over the bar {bar}"
     return m
+
+
+def oracle_with_floor(x, weights, names=("z", "k", "v"), **kw):
+    """The oracle's bf16-mode layer outputs, and its own noise floor per output: the
+    same layer with every weight multiplied by (1 + PERTURB N(0,1)), stored (rounded
+    to bf16), against the unperturbed values before rounding; the max of that
+    difference over |ref| < 4. Returns (ref, floor dict)."""
+    import oracle
+    ref = oracle.layer_forward(x, weights, round_bf16=True, **kw)
+    rng = np.random.default_rng(4242)
+    wp = {k: (np.asarray(v, dtype=np.float64) * (1.0 + PERTURB * rng.standard_normal(np.shape(v)))).astype(np.float32)
+          if (k.startswith("w_") and v is not None) else v for k, v in weights.items()}
+    per = oracle.layer_forward(x, wp, round_bf16=True, **kw)
+    floor = {}
+    for nm in names:
+        r = ref[nm]
+        small = np.abs(r) < BIG
+        d = np.abs(oracle.round_bf16(per[nm]) - r)
+        floor[nm] = float(d[small].max()) if small.any() else 0.0
+    return ref, floor
 
 
 def bf16_ulp(x) -> np.ndarray:
@@ -84,9 +132,10 @@ def attn_desc(batch, n_pos, n_heads, head_dim, dt, scale):
                        softmax_scale=scale)
 
 
-def layer_desc(batch, n_pos, d_model, n_heads, d_ff, dt, scale, eps=1e-6, rho=1.0, flags=0):
+def layer_desc(batch, n_pos, d_model, n_heads, d_ff, dt, scale, eps=1e-6, rho=1.0, flags=0, kv_source_norm=1):
     a = attn_desc(batch, n_pos, n_heads, d_model // n_heads, dt, scale)
-    return rt.LayerDesc(attn=a, d_model=d_model, d_ff=d_ff, rms_eps=eps, residual_scale=rho, flags=flags)
+    return rt.LayerDesc(attn=a, d_model=d_model, d_ff=d_ff, rms_eps=eps, residual_scale=rho, flags=flags,
+                        kv_source_norm=kv_source_norm)
 
 
 def run_attention_sequence(desc, q, ke, ve, k, v, state_fill=None):

@@ -137,8 +137,9 @@ def test_workspace_bytes(lib):
     D = h * dh
     al = lambda x: (x + 255) // 256 * 256
     want = 3 * al(n * b * D * 2) + 2 * al(n * b * h * 4) + al(n * b * D * 4) + al(b * D * 2) + al(b * D * 4) \
-        + al(b * f * 2) + al(b * D * 2) + 2 * al(D // 32 * b * 4 + 4) + 3 * al(D * D * 2) + al(f * D * 2) \
-        + al(n * b * 16)  # quarter-row sums of x^2 for the up-front projection
+        + al(b * f * 2) + al(b * D * 2) + 2 * al(D // 32 * b * 4 + 4) \
+        + 3 * al(2 * D * D * 2) + al(2 * f * D * 2) \
+        + al(n * b * 16)  # gain-folded bf16 weights (two halves per row); quarter-row sums of x^2
     assert rt.rt_layer_workspace_bytes(d) == want
     assert rt.rt_layer_workspace_bytes(_layer(d_model=100)) == 0
     assert rt.rt_layer_workspace_bytes(_layer(d_ff=100)) == 0  # bf16 needs multiples of 128
@@ -148,7 +149,7 @@ def test_workspace_bytes_of_the_other_modes(lib):
     n, b, h, dh, f = 16, 2, 2, 64, 256
     D = h * dh
     al = lambda x: (x + 255) // 256 * 256
-    weights = 3 * al(D * D * 2) + al(f * D * 2)
+    weights = 3 * al(2 * D * D * 2) + al(2 * f * D * 2)  # gain-folded bf16 weights, two halves per row
     xss = lambda rows: al(rows * 16)  # quarter-row sums of x^2 for the up-front projection
 
     def tail(rows):  # a, h, g, hb, hss, zss
@@ -186,6 +187,24 @@ def test_flags_are_validated(lib):
         rt.rt_layer_forward(_layer(flags=rt.RT_FLAG_QK_NORM), dict(W, g_q=FAKE + 4), FAKE, FAKE, FAKE, FAKE, FAKE,
                             1 << 30, stream=0)
     assert "aligned" in str(e.value)
+
+
+def test_kv_source_norm_is_validated(lib):
+    W = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    assert _layer().kv_source_norm == 1  # the binding's default: the persistent pair reads RMS_attn(z)
+    lit = _layer(kv_source_norm=0)
+    assert rt.rt_layer_workspace_bytes(lit) == rt.rt_layer_workspace_bytes(_layer())
+    for bad, text in ((_layer(kv_source_norm=2), "0 or 1"),
+                      (_layer(kv_source_norm=0, flags=rt.RT_FLAG_TRANSFORMER), "ephemeral")):
+        assert rt.rt_layer_workspace_bytes(bad) == 0
+        with pytest.raises(rt.RtError) as e:
+            rt.rt_layer_forward(bad, W, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, stream=0)
+        assert e.value.status == 1 and text in str(e.value)
+    G = {n: FAKE for n in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
+    assert rt.rt_layer_backward_workspace_bytes(lit) == 0
+    with pytest.raises(rt.RtError) as e:
+        rt.rt_layer_backward(lit, W, FAKE, FAKE, FAKE, FAKE, G, FAKE, 1 << 30, stream=0)
+    assert e.value.status == 2
 
 
 def test_decode_rejects_bad_arguments(lib):

@@ -1,21 +1,21 @@
 """GPU parity of the RT layer's backward (rt_layer_backward) against the
-oracle's gradient (oracle/layer_backward.py, fp64, exact layer), through the
-C ABI. The GPU runs the layer forward first and differentiates from its own
-stored output z, as a caller would.
+oracle's gradient (oracle/layer_backward.py, fp64), through the C ABI.
+
+The backward is evaluated at a forward pass; data flows from the oracle to
+the GPU only: the GPU's rt_layer_backward reads the oracle's own stored
+output z (its bf16 values in bf16 layers) as the forward it differentiates,
+and the oracle takes its derivatives at its own forward values, in bf16
+layers as a bf16 layer stores them (q, k', v', k, v, a, z, the MLP's
+pre-activation and activation, the normalised inputs of the weight products;
+round_bf16 of layer_backward).
 
 Inputs are seeded and synthetic: x ~ N(0,1), weights N(0, 1/d_in), gains
 1 + 0.3 N(0,1) where present, z_bar ~ N(0,1).
 
-Bars, relative L2 of each gradient against the oracle's:
-  - fp32 layers 1e-5: fp32 arithmetic throughout, sums over up to N*B*F
-    terms (weight gradients) and a chain of N reverse steps (measured
-    2.5e-7 .. 5e-7);
-  - bf16 layers 2.5e-2: the forward's stored values (q, k', v', a, the MLP
-    activation, z, k, v) are bf16, each a 2^-9 relative rounding the exact
-    oracle does not make, and every adjoint product reads its operands
-    rounded to bf16 (another 2^-9 each); a gradient passes through ~6 such
-    roundings per reverse step, independent across steps and elements, so
-    the relative error lands near 1e-2 (measured 3e-3 .. 1.05e-2).
+Bar, relative L2 of each gradient against the oracle's: 1e-5 in fp32
+layers, 5e-3 in bf16 layers (the stated bf16 bar; what remains is the bf16
+rounding of the adjoints where a product reads them, 2^-9 relative each,
+and the rounding decisions of the recomputed forward values).
 """
 import math
 
@@ -23,12 +23,13 @@ import numpy as np
 import pytest
 
 import blocked_prefill_amd as rt
+import rt_inputs
 from oracle.layer_backward import layer_backward
 from tests import gpu_util as G
 
 pytestmark = pytest.mark.gpu
 
-BAR = {"f32": 1e-5, "bf16": 2.5e-2}
+BAR = {"f32": 1e-5, "bf16": 5e-3}
 NAMES = ("x", "w_q", "w_k", "w_v", "w_o", "w_1", "w_2", "g_attn", "g_mlp")
 
 
@@ -57,10 +58,18 @@ def _case(seed, n, b, d, f, gains):
 def _run(dt, n, b, d, heads, f, rho, gains, seed):
     import torch
     x, w, z_bar = _case(seed, n, b, d, f, gains)
+    if dt == "bf16":
+        x = rt_inputs.to_storage(x, dt)
+        w = {k: (rt_inputs.to_storage(v, dt) if k.startswith("w_") else v) for k, v in w.items()}
     scale = 1.0 / math.sqrt(d // heads)
     desc = G.layer_desc(b, n, d, heads, f, dt, scale, rho=rho)
+    ref = layer_backward(x, w, z_bar.astype(np.float64), n_heads=heads, softmax_scale=scale, residual_scale=rho,
+                         round_bf16=(dt == "bf16"))
     buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt, gains=gains)
-    buf.forward()
+    if dt == "bf16":
+        buf.z = G.dev(ref["z_stored"], dt)  # the forward being differentiated: the oracle's stored output
+    else:
+        buf.forward()
     f32 = dict(dtype=torch.float32, device="cuda")
     grads = {k: torch.full(w[k].shape, float("nan"), **f32) for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
     grads["g_attn"] = torch.full((d,), float("nan"), **f32)
@@ -72,7 +81,6 @@ def _run(dt, n, b, d, heads, f, rho, gains, seed):
     zb = torch.from_numpy(z_bar).cuda()
     rt.rt_layer_backward(desc, buf.w, buf.x, buf.z, zb, x_bar, grads, ws)
     torch.cuda.synchronize()
-    ref = layer_backward(x, w, z_bar.astype(np.float64), n_heads=heads, softmax_scale=scale, residual_scale=rho)
     got = {"x": G.host(x_bar), **{k: G.host(v) for k, v in grads.items()}}
     return got, ref
 
@@ -110,8 +118,11 @@ def test_layer_backward_full_size_two_rows():
     z_bar[:, rows] = np.random.default_rng(78).standard_normal((n, len(rows), d)).astype(np.float32)
     scale = 1.0 / math.sqrt(d // heads)
     desc = G.layer_desc(b, n, d, heads, f, "bf16", scale)
+    ref = layer_backward(x[:, rows], w, z_bar[:, rows].astype(np.float64), n_heads=heads, softmax_scale=scale,
+                         round_bf16=True)
     buf = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16")
-    buf.forward()
+    buf.forward()  # the other rows' forward; the two rows take the oracle's stored output
+    buf.z[:, torch.tensor(rows, device="cuda")] = G.dev(ref["z_stored"], "bf16")
     f32 = dict(dtype=torch.float32, device="cuda")
     grads = {k: torch.empty(w[k].shape, **f32) for k in w}
     x_bar = torch.empty((n, b, d), **f32)
@@ -124,7 +135,6 @@ def test_layer_backward_full_size_two_rows():
     others[rows] = False
     assert np.all(xb[:, others] == 0.0)
     del ws, buf
-    ref = layer_backward(x[:, rows], w, z_bar[:, rows].astype(np.float64), n_heads=heads, softmax_scale=scale)
     got = {"x": xb[:, rows], **{k: G.host(v) for k, v in grads.items()}}
     for name in ("x", "w_q", "w_k", "w_v", "w_o", "w_1", "w_2"):
         rel = float(np.linalg.norm(got[name] - ref[name]) / max(np.linalg.norm(ref[name]), 1e-300))

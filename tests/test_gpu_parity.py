@@ -10,6 +10,7 @@ import math
 import numpy as np
 import pytest
 
+import blocked_prefill_amd as rt
 import oracle
 import rt_inputs
 from tests import gpu_util as G
@@ -114,11 +115,11 @@ def _small_weights(seed, d, f, dt, gains):
 
 
 def _compare_layer(buf, x_rows, w_np, rows, dt, n_heads, scale, rho=1.0, what="layer"):
-    ref = oracle.layer_forward(x_rows, w_np, n_heads=n_heads, softmax_scale=scale, residual_scale=rho,
-                               round_bf16=(dt == "bf16"))
+    kw = dict(n_heads=n_heads, softmax_scale=scale, residual_scale=rho)
+    ref, floor = G.oracle_with_floor(x_rows, w_np, **kw) if dt == "bf16" else (oracle.layer_forward(x_rows, w_np, **kw), {})
     out = {}
     for name, t in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
-        out[name] = G.parity(G.host(t)[:, rows], ref[name], dt, f"{what}.{name}")
+        out[name] = G.parity(G.host(t)[:, rows], ref[name], dt, f"{what}.{name}", floor=floor.get(name))
     return ref, out
 
 
@@ -135,8 +136,11 @@ def test_layer_tiny_f32_all_rows():
 
 
 @pytest.mark.parametrize("dt,n,b,d,h,f", [("f32", 50, 3, 96, 3, 128), ("bf16", 100, 5, 256, 4, 512),
-                                           ("bf16", 33, 2, 256, 2, 384)])
+                                           ("bf16", 33, 2, 256, 2, 384), ("bf16", 300, 3, 256, 4, 512)])
 def test_layer_small_with_gains_and_residual_scale(dt, n, b, d, h, f):
+    """Non-unit RMS gains and rho = 0.7 against the oracle given the same
+    weights and gains (the library folds each gain into the following
+    projection in fp32, kept in bf16 as two halves)."""
     rng = np.random.default_rng(n)
     x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), dt)
     w = _small_weights(n + 1, d, f, dt, gains=True)
@@ -144,14 +148,57 @@ def test_layer_small_with_gains_and_residual_scale(dt, n, b, d, h, f):
     desc = G.layer_desc(b, n, d, h, f, dt, scale, rho=0.7)
     buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt, gains=True)
     buf.forward()
-    # the library folds the gains into the projection weights, stored in the layer's dtype
-    w_fold = dict(w)
+    _, m = _compare_layer(buf, x, w, list(range(b)), dt, h, scale, rho=0.7)
+    print(f"gains {dt} N={n}: {m}")
+
+
+@pytest.mark.parametrize("dt,n,flags", [("bf16", 100, 0), ("f32", 40, 0), ("bf16", 70, rt.RT_FLAG_NAIVE_SCHEDULE),
+                                        ("bf16", 60, rt.RT_FLAG_QK_NORM)])
+def test_layer_literal_kv_source(dt, n, flags):
+    """kv_source_norm = 0: the persistent pair is W_k z_t, W_v z_t (the literal
+    reading of the cut formula), against the oracle's literal reading."""
+    b, d, h, f = 3, 256, 4, 512
+    if dt == "f32":
+        d, h, f = 96, 3, 128
+    rng = np.random.default_rng(200 + n)
+    x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), dt)
+    w = _small_weights(n + 1, d, f, dt, gains=True)
+    scale = 1.0 / math.sqrt(d // h)
+    qk = bool(flags & rt.RT_FLAG_QK_NORM)
+    if qk:
+        w["g_q"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+        w["g_k"] = (1 + 0.3 * rng.standard_normal(d)).astype(np.float32)
+    desc = G.layer_desc(b, n, d, h, f, dt, scale, rho=0.9, flags=flags, kv_source_norm=0)
+    buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt, gains=True)
+    buf.forward()
+    kw = dict(n_heads=h, softmax_scale=scale, residual_scale=0.9, qk_norm=qk, kv_source_norm=False)
     if dt == "bf16":
-        for n_, g in (("w_q", "g_attn"), ("w_k", "g_attn"), ("w_v", "g_attn"), ("w_1", "g_mlp")):
-            w_fold[n_] = rt_inputs.to_storage(w[n_] * w[g][None, :], dt)
-        w_fold["g_attn"] = None
-        w_fold["g_mlp"] = None
-    _compare_layer(buf, x, w_fold, list(range(b)), dt, h, scale, rho=0.7)
+        ref, floor = G.oracle_with_floor(x, w, **kw)
+    else:
+        ref, floor = oracle.layer_forward(x, w, **kw), {}
+    for name, t_ in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
+        m = G.parity(G.host(t_), ref[name], dt, f"literal.{name}", floor=floor.get(name))
+        print(f"literal kv source {dt} flags={flags}: {name} {m}")
+
+
+def test_layer_rows_permute_with_the_batch():
+    """Batch rows are independent (position-major layout, strides per row):
+    permuting the rows of x permutes every output row for row, bit for bit."""
+    import torch
+    n, b, d, h, f = 70, 24, 256, 4, 512  # B > 16: the small steps run inside the K/V product
+    rng = np.random.default_rng(17)
+    x = rt_inputs.to_storage(rng.standard_normal((n, b, d)).astype(np.float32), "bf16")
+    w = _small_weights(18, d, f, "bf16", gains=True)
+    perm = rng.permutation(b)
+    desc = G.layer_desc(b, n, d, h, f, "bf16", 0.125)
+    one = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16", gains=True)
+    one.forward()
+    two = G.LayerBuffers(desc, G.dev(x[:, perm], "bf16"), w, "bf16", gains=True)
+    two.forward()
+    torch.cuda.synchronize()
+    p = torch.tensor(perm, device="cuda")
+    for name in ("z", "k", "v"):
+        assert torch.equal(getattr(one, name)[:, p], getattr(two, name)), name
 
 
 @pytest.mark.parametrize("n", [40, 130])
@@ -239,11 +286,11 @@ def _full_layer(name, rows, use_plan=True):
     for layer in range(wl.n_layers):
         w = rt_inputs.layer_weights(wl, layer)
         desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, dt, scale)
-        ref = oracle.layer_forward(x_rows, w, n_heads=wl.n_heads, softmax_scale=scale, round_bf16=(dt == "bf16"))
+        ref, floor = G.oracle_with_floor(x_rows, w, n_heads=wl.n_heads, softmax_scale=scale)
         xin = chain_dev.clone()
         xin[:, idx] = G.dev(x_rows, dt)
         same = _run_layer(desc, xin, w, dt, use_plan)
-        m = {nm: G.parity(G.host(t_[:, idx]), ref[nm], dt, f"{name}[layer {layer}].{nm}")
+        m = {nm: G.parity(G.host(t_[:, idx]), ref[nm], dt, f"{name}[layer {layer}].{nm}", floor=floor[nm])
              for nm, t_ in (("z", same.z), ("k", same.k), ("v", same.v))}
         per_layer.append(m)
         print(f"{name} layer {layer} on identical inputs: {m}")
@@ -273,21 +320,33 @@ def test_stack_full_d1024_b512_n2048_six_layers():
     _full_layer("stack6_d1024_b512_n2048", rows=[0, 511])
 
 
-def test_layer_long_b8_n32768_prefix():
-    """B=8, N=32768: the layer's positions 1..1024 of two rows (outputs there depend
-    only on earlier positions) plus finiteness of every output."""
+def test_layer_long_b8_n32768_through_the_plan():
+    """B=8, N=32768 through the layer plan (the bench's launch configuration: a
+    chain of 12 HIP graphs). Row 7, positions 1..4096, against the oracle run
+    live (outputs there depend only on earlier positions; blocks of up to 2048
+    pairs reach them); row 0 at 16 positions up to 32768 (blocks up to 16384)
+    against the oracle's stored values (tests/golden/make_long_layer_golden.py);
+    every output finite."""
+    import os
     import torch
     wl = rt_inputs.WORKLOADS["long_d1024_b8_n32768"]
     scale = 1.0 / math.sqrt(wl.head_dim)
     x = rt_inputs.layer_input(wl)
     w = rt_inputs.layer_weights(wl, 0)
+    w = {k: w[k] for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")}
     desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, "bf16", scale)
-    buf = G.LayerBuffers(desc, G.dev(x, "bf16"), w, "bf16")
-    buf.forward()
-    torch.cuda.synchronize()
+    buf = _run_layer(desc, G.dev(x, "bf16"), w, "bf16", use_plan=True)
     for t_ in (buf.z, buf.k, buf.v):
         assert bool(torch.isfinite(t_).all())
-    rows, T = [0, 7], 1024
-    ref = oracle.layer_forward(x[:T, rows], w, n_heads=wl.n_heads, softmax_scale=scale, round_bf16=True)
+    gold = np.load(os.path.join(os.path.dirname(__file__), "golden", "long_d1024_b8_n32768_row0.npz"))
+    sel = gold["positions"].astype(np.int64) - 1
     for name, t_ in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
-        G.parity(G.host(t_[:T])[:, rows], ref[name], "bf16", f"long.{name}")
+        m = G.parity(G.host(t_[torch.tensor(sel, device="cuda"), 0]), gold[name].astype(np.float64), "bf16",
+                     f"long row 0, stored positions .{name}")
+        print(f"long.{name} at positions {gold['positions'].tolist()}: {m}", flush=True)
+    T, rows = 4096, [7]
+    ref, floor = G.oracle_with_floor(x[:T, rows], w, n_heads=wl.n_heads, softmax_scale=scale)
+    for name, t_ in (("z", buf.z), ("k", buf.k), ("v", buf.v)):
+        m = G.parity(G.host(t_[:T, rows]), ref[name], "bf16", f"long row 7, positions 1..{T}.{name}",
+                     floor=floor[name])
+        print(f"long.{name} positions 1..{T}: {m}", flush=True)

@@ -123,35 +123,41 @@ def test_stack_f32_equals_layer_by_layer(n):
 
 
 @pytest.mark.parametrize("n,qk,rho,gains,h", [(100, False, 1.0, True, 4), (100, False, 1.0 / math.sqrt(6.0), True, 4),
-                                             (100, True, 1.0, False, 4), (100, False, 1.0, True, 8)])
+                                             (100, True, 1.0, True, 4), (100, False, 1.0, True, 8),
+                                             (300, False, 1.0, True, 4), (300, True, 1.0, True, 4)])
 def test_stack_bf16_each_layer_matches_oracle(n, qk, rho, gains, h):
-    """Each layer on its actual input (the stack's previous output): against the
-    oracle (the parity bars) and against the single-layer path. N=100 has chunks
-    of 8 positions: steps of 16..64 pairs defer rows. (The bf16 recurrence
-    amplifies rounding flips with N: at N=300 the single-layer path itself sits
-    at the max-abs bar on some seeds, 0.0204 beyond the half-ulp, with the
-    stack within 3e-6 of it there. The query/key norm runs without the RMS
-    gains, as in the single-layer tests: bf16 layers fold a gain into the
-    weights, rounded to bf16, and the per-head norm amplifies that rounding
-    where a head's vector is small; with both, the single-layer path itself
-    reaches 0.028 beyond the half-ulp on this case, the stack equal to it.)"""
-    dt, b, d, f, L = "bf16", 3, 256, 512, 3  # h = 8: head_dim 32, whose small steps run per layer
+    """Every layer of a bf16 stack, with data flowing from the oracle to the GPU only:
+    - the oracle runs its own chain (layer l reads its own stored output of layer l-1);
+    - the library's single-layer path on the oracle's input of layer l meets the bars
+      against the oracle's layer l;
+    - the stack's layer l meets the bars against the single-layer path on the stack's
+      own input of layer l (the wavefront's grouped products and deferred rows against
+      one layer's launches);
+    - the stack's layer 0 (same input as the oracle's) meets the bars against it.
+    N=100 has chunks of 8 positions (steps of 16..64 pairs defer rows); N=300 chunks
+    of 16 (steps of 32..256). h = 8: head_dim 32, whose small steps run per layer."""
+    dt, b, d, f, L = "bf16", 3, 256, 512, 3
     flags = rt.RT_FLAG_QK_NORM if qk else 0
     x, ws, scale, desc = _case(dt, n, b, d, h, f, L, seed=20 + n, qk=qk, flags=flags, rho=rho, gains=gains)
     st = _run_stack(desc, x, ws, dt)
-    x_host = x.astype(np.float64)
-    x_dev = st.x
+    x_oracle = x
     for i in range(L):
-        ref = oracle.layer_forward(x_host, ws[i], n_heads=h, softmax_scale=scale, residual_scale=rho,
-                                   round_bf16=True, qk_norm=qk)
-        one = _layer(desc, x_dev, ws[i], dt)
+        ref, floor = G.oracle_with_floor(x_oracle, ws[i], n_heads=h, softmax_scale=scale, residual_scale=rho,
+                                         qk_norm=qk)
+        on_oracle_input = _layer(desc, G.dev(x_oracle, dt), ws[i], dt)
+        on_stack_input = _layer(desc, st.x if i == 0 else st.z[i - 1], ws[i], dt)
         for name in ("z", "k", "v"):
-            got = G.host(getattr(st, name)[i])
-            m = G.parity(got, ref[name], dt, f"stack layer {i}.{name} vs oracle")
-            s = G.parity(got, G.host(getattr(one, name)), dt, f"stack layer {i}.{name} vs single layer")
-            print(f"layer {i}.{name}: oracle {m}, single layer {s}")
-        x_host = G.host(st.z[i])
-        x_dev = st.z[i]
+            m = G.parity(G.host(getattr(on_oracle_input, name)), ref[name], dt, f"layer {i}.{name} vs oracle",
+                         floor=floor[name])
+            # two bf16 results of the same layer (the oracle's floor of this layer stands for the
+            # noise between two rounding orders)
+            s_ = G.parity(G.host(getattr(st, name)[i]), G.host(getattr(on_stack_input, name)), dt,
+                          f"stack layer {i}.{name} vs single layer", floor=floor[name], stored=True)
+            if i == 0:
+                G.parity(G.host(getattr(st, name)[0]), ref[name], dt, f"stack layer 0.{name} vs oracle",
+                         floor=floor[name])
+            print(f"layer {i}.{name}: single layer vs oracle {m}; stack vs single layer {s_}")
+        x_oracle = ref["x_next"]
 
 
 def test_stack_plan_replays_match_eager():
@@ -190,26 +196,40 @@ def test_stack_other_modes_equal_layer_by_layer(flags, n_layers):
 
 def test_stack_full_d1024_b512_n2048_six_layers():
     """The 6-layer stack at full size (B=512, N=2048, d=1024, bf16) through the
-    stack plan, as the benchmark runs it; each layer's sampled batch rows against
-    the oracle on that layer's actual input (rows are independent)."""
+    stack plan, as the benchmark runs it. Layer 0 reads the same input as the
+    oracle: its sampled batch rows against the oracle. Every layer against the
+    single-layer plan on the stack's own input of that layer (sampled rows; the
+    single-layer path on the oracle's own chain is checked against the oracle
+    layer by layer in test_gpu_parity)."""
     import torch
     wl = rt_inputs.WORKLOADS["stack6_d1024_b512_n2048"]
-    rows = [0, 511]
+    rows = [0, 1, 255, 511]
     scale = 1.0 / math.sqrt(wl.head_dim)
     desc = G.layer_desc(wl.batch, wl.n_pos, wl.d_model, wl.n_heads, wl.d_ff, "bf16", scale)
     x = rt_inputs.layer_input(wl)
     weights = [rt_inputs.layer_weights(wl, i) for i in range(wl.n_layers)]
+    weights = [{k: w[k] for k in ("w_q", "w_k", "w_v", "w_o", "w_1", "w_2")} for w in weights]
     st = StackBuffers(desc, G.dev(x, "bf16"), weights, "bf16")
     del x
     plan = st.plan()
     plan.launch()
     torch.cuda.synchronize()
     plan.destroy()
+    del st.ws
     idx = torch.tensor(rows, device="cuda")
-    x_rows = rt_inputs.layer_input(wl, rows=rows).astype(np.float64)
+    x_rows = rt_inputs.layer_input(wl, rows=rows[:2]).astype(np.float64)
+    ref, floor = G.oracle_with_floor(x_rows, weights[0], n_heads=wl.n_heads, softmax_scale=scale)
+    m = {nm: G.parity(G.host(getattr(st, nm)[0][:, idx[:2]]), ref[nm], "bf16", f"stack layer 0.{nm} vs oracle",
+                      floor=floor[nm]) for nm in ("z", "k", "v")}
+    print(f"stack layer 0 vs oracle: {m}", flush=True)
     for i in range(wl.n_layers):
-        ref = oracle.layer_forward(x_rows, weights[i], n_heads=wl.n_heads, softmax_scale=scale, round_bf16=True)
-        m = {nm: G.parity(G.host(getattr(st, nm)[i][:, idx]), ref[nm], "bf16", f"stack layer {i}.{nm}")
+        buf = G.LayerBuffers(desc, st.x if i == 0 else st.z[i - 1], weights[i], "bf16")
+        p = buf.plan()
+        p.launch()
+        torch.cuda.synchronize()
+        p.destroy()
+        m = {nm: G.parity(G.host(getattr(st, nm)[i][:, idx]), G.host(getattr(buf, nm)[:, idx]), "bf16",
+                          f"stack layer {i}.{nm} vs single layer", floor=floor[nm], stored=True)
              for nm in ("z", "k", "v")}
-        print(f"stack layer {i}: {m}", flush=True)
-        x_rows = G.host(st.z[i][:, idx])
+        print(f"stack layer {i} vs the single-layer plan on its input: {m}", flush=True)
+        del buf

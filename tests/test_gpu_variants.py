@@ -43,7 +43,7 @@ def _input(seed, n, b, d, dt):
 
 def _forward(desc, x, w, dt):
     import torch
-    buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt)
+    buf = G.LayerBuffers(desc, G.dev(x, dt), w, dt, gains="g_attn" in w)
     buf.forward()
     torch.cuda.synchronize()
     return buf
@@ -121,15 +121,20 @@ def _qk_gains(w, seed, d):
     ("bf16", 40, 2, 256, 4, 512, 2),                           # naive schedule
 ])
 def test_qk_norm_layer_matches_oracle(dt, n, b, d, h, f, flags):
-    """Per-head query/key norm with non-unit gains, on every layer mode."""
+    """Per-head query/key norm with non-unit gains (and non-unit RMS gains g_attn,
+    g_mlp), on every layer mode."""
     x = _input(3 * n, n, b, d, dt)
     w = _qk_gains(_weights(n + 11, d, f, dt), n, d)
+    rng = np.random.default_rng(n + 12)
+    w["g_attn"] = (1 + 0.2 * rng.standard_normal(d)).astype(np.float32)
+    w["g_mlp"] = (1 + 0.2 * rng.standard_normal(d)).astype(np.float32)
     scale = 1.0 / math.sqrt(d // h)
     buf = _forward(G.layer_desc(b, n, d, h, f, dt, scale, flags=flags | rt.RT_FLAG_QK_NORM), x, w, dt)
-    ref = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale, round_bf16=(dt == "bf16"), qk_norm=True,
-                               kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER))
+    kw = dict(n_heads=h, softmax_scale=scale, qk_norm=True, kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER))
+    ref, floor = G.oracle_with_floor(x, w, **kw) if dt == "bf16" else (oracle.layer_forward(x, w, **kw), {})
     for name in ("z", "k", "v"):
-        G.parity(G.host(getattr(buf, name)), ref[name], dt, f"qk_norm[{flags}].{name}")
+        m = G.parity(G.host(getattr(buf, name)), ref[name], dt, f"qk_norm[{flags}].{name}", floor=floor.get(name))
+        print(f"qk_norm[{flags}] {dt} N={n}: {name} {m}")
 
 
 def _decode_case(dt, n_past, steps, b, d, h, f, flags=0, seed=0, scale=None):
@@ -161,36 +166,44 @@ def _decode_case(dt, n_past, steps, b, d, h, f, flags=0, seed=0, scale=None):
     for i in range(steps):
         rt.rt_layer_decode_step(desc, W, n_past + i, x_dev[n_past + i], z[i], kc, vc, ws)
     torch.cuda.synchronize()
-    ref = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale, round_bf16=(dt == "bf16"),
-                               kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER),
-                               qk_norm=bool(flags & rt.RT_FLAG_QK_NORM))
+    kw = dict(n_heads=h, softmax_scale=scale, kv_from_input=bool(flags & rt.RT_FLAG_TRANSFORMER),
+              qk_norm=bool(flags & rt.RT_FLAG_QK_NORM))
+    if dt == "bf16":
+        ref, floor = G.oracle_with_floor(x, w, **kw)
+    else:
+        ref, floor = oracle.layer_forward(x, w, **kw), {}
+    ref["floor"] = floor
     return G.host(z), G.host(kc), G.host(vc), ref
 
 
 @pytest.mark.parametrize("dt,n_past,h,scale", [
-    ("bf16", 0, 4, None), ("bf16", 1, 4, None), ("bf16", 31, 4, None), ("bf16", 32, 4, None),
+    ("bf16", 0, 4, None), ("bf16", 1, 4, None), ("bf16", 14, 4, None), ("bf16", 31, 4, None), ("bf16", 32, 4, None),
     ("bf16", 45, 4, None), ("bf16", 129, 4, None), ("bf16", 100, 8, None), ("f32", 37, 4, None),
     ("bf16", 45, 4, 0.0),
 ])
 def test_decode_steps_match_oracle(dt, n_past, h, scale):
     """Decode after a prefill of n_past positions (none, fewer than 32, ragged
     multiples of the 64-position tile), three positions in a row; softmax_scale
-    0 (uniform weights) also across the masked rows of a ragged tile."""
+    0 (uniform weights) also across the masked rows of a ragged tile. n_past = 14:
+    the third step reads 16 cached pairs, the two-pairs-per-wave kernel with no
+    stored state (a null-state step of 8 or 16 pairs once faulted there)."""
     steps, b, d, f = 3, 3, 256, 512
     z, kc, vc, ref = _decode_case(dt, n_past, steps, b, d, h, f, scale=scale)
     n = n_past + steps
-    G.parity(z, ref["z"][n_past:], dt, f"decode.z (n_past={n_past})")
-    G.parity(kc, ref["k"], dt, f"decode.k_cache (n_past={n_past})")
-    G.parity(vc, ref["v"], dt, f"decode.v_cache (n_past={n_past})")
+    fl = ref["floor"]
+    G.parity(z, ref["z"][n_past:], dt, f"decode.z (n_past={n_past})", floor=fl.get("z"))
+    G.parity(kc, ref["k"], dt, f"decode.k_cache (n_past={n_past})", floor=fl.get("k"))
+    G.parity(vc, ref["v"], dt, f"decode.v_cache (n_past={n_past})", floor=fl.get("v"))
     assert kc.shape[0] == n
 
 
 def test_qk_norm_decode_steps_match_oracle():
     steps, b, d, h, f, n_past = 3, 2, 256, 4, 512, 45
     z, kc, vc, ref = _decode_case("bf16", n_past, steps, b, d, h, f, flags=rt.RT_FLAG_QK_NORM, seed=9)
-    G.parity(z, ref["z"][n_past:], "bf16", "qk_norm decode.z")
-    G.parity(kc, ref["k"], "bf16", "qk_norm decode.k_cache")
-    G.parity(vc, ref["v"], "bf16", "qk_norm decode.v_cache")
+    fl = ref["floor"]
+    G.parity(z, ref["z"][n_past:], "bf16", "qk_norm decode.z", floor=fl["z"])
+    G.parity(kc, ref["k"], "bf16", "qk_norm decode.k_cache", floor=fl["k"])
+    G.parity(vc, ref["v"], "bf16", "qk_norm decode.v_cache", floor=fl["v"])
 
 
 @pytest.mark.parametrize("n_past", [0, 50])
