@@ -16,8 +16,8 @@ __all__ = [
     "rt_layer_forward", "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
     "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
     "rt_layer_backward_workspace_bytes", "rt_layer_backward", "LayerGrads", "rt_last_error", "EXPORTED",
-    "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create",
-    "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
+    "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create", "rt_layer_decode_step_static",
+    "RT_DECODE_STATIC_SCRATCH_BYTES", "RT_FLAG_DEBUG_SYNC", "RT_FLAG_NAIVE_SCHEDULE", "RT_FLAG_TRANSFORMER", "RT_FLAG_QK_NORM",
 ]
 
 RT_F32, RT_BF16 = 0, 1
@@ -25,6 +25,7 @@ RT_FLAG_DEBUG_SYNC = 1
 RT_FLAG_NAIVE_SCHEDULE = 2
 RT_FLAG_TRANSFORMER = 4
 RT_FLAG_QK_NORM = 8
+RT_DECODE_STATIC_SCRATCH_BYTES = 64 << 20  # rt_layer_decode_step_static's scratch (include/rt_prefill.h)
 _STATUS = {0: "RT_OK", 1: "RT_ERR_INVALID_ARG", 2: "RT_ERR_UNSUPPORTED", 3: "RT_ERR_WORKSPACE", 4: "RT_ERR_HIP",
            5: "RT_ERR_INTERNAL"}
 
@@ -36,7 +37,7 @@ EXPORTED = ["rt_blocked_attn_update", "rt_finalize_step", "rt_update_finalize_st
             "rt_layer_plan_create", "rt_layer_plan_launch", "rt_layer_plan_destroy", "rt_schedule_step",
             "rt_layer_decode_workspace_bytes", "rt_layer_decode_step", "rt_attn_forward", "rt_attn_backward",
             "rt_layer_backward_workspace_bytes", "rt_layer_backward", "rt_last_error",
-            "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create"]
+            "rt_stack_workspace_bytes", "rt_stack_forward", "rt_stack_plan_create", "rt_layer_decode_step_static"]
 
 
 class RtError(RuntimeError):
@@ -94,6 +95,8 @@ def load():
             "rt_attn_backward": [ctypes.POINTER(AttnDesc)] + [_vp] * 15,
             "rt_layer_decode_step": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _i32, _vp, _vp, _vp,
                                      _vp, _vp, ctypes.c_size_t, _vp],
+            "rt_layer_decode_step_static": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _i32, _vp,
+                                            _vp, _vp, _vp, _vp],
             "rt_schedule_step": [_i32, _i32] + [ctypes.POINTER(_i32)] * 4,
             "rt_layer_backward": [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), _vp, _vp, _vp, _vp,
                                   ctypes.POINTER(LayerGrads), _vp, ctypes.c_size_t, _vp],
@@ -212,6 +215,13 @@ def rt_layer_decode_step(desc: LayerDesc, weights, n_past: int, x_t, z_t, k_cach
     W = _weights(weights)
     _check(load().rt_layer_decode_step(ctypes.byref(desc), ctypes.byref(W), n_past, _ptr(x_t), _ptr(z_t),
                                        _ptr(k_cache), _ptr(v_cache), _ptr(workspace), ws, _stream(stream)))
+
+
+def rt_layer_decode_step_static(desc: LayerDesc, weights, n_past: int, x_t, z_t, k_cache, v_cache, stream=None):
+    """rt_layer_decode_step with the library's own static scratch (no workspace, no allocation)."""
+    W = _weights(weights)
+    _check(load().rt_layer_decode_step_static(ctypes.byref(desc), ctypes.byref(W), n_past, _ptr(x_t), _ptr(z_t),
+                                              _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def rt_layer_backward_workspace_bytes(desc: LayerDesc) -> int:

@@ -992,6 +992,23 @@ rt_status capture_plan(F&& enqueue, rt_plan** plan) {
 
 }  // namespace
 
+namespace rt {
+
+rt_status set_error(rt_status st, const char* a, const char* b) { return fail(st, "%s%s", a, b); }
+
+rt_status check_decode_args(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past, const void* x_t,
+                            void* z_t, void* k_cache, void* v_cache) {
+    RT_TRY(check_layer(desc));
+    // (the workspace is checked by the caller; a stand-in aligned address here)
+    RT_TRY(check_layer_ptrs(w, x_t, z_t, k_cache, v_cache, reinterpret_cast<void*>(uintptr_t(256))));
+    if (n_past < 0 || n_past >= desc->attn.seq_len)
+        return fail(RT_ERR_INVALID_ARG, "n_past=%d outside 0..%d (seq_len is the cache capacity)", n_past,
+                    desc->attn.seq_len - 1);
+    return RT_OK;
+}
+
+}  // namespace rt
+
 extern "C" {
 
 const char* rt_last_error(void) { return g_last_error.c_str(); }
@@ -1189,11 +1206,8 @@ size_t rt_layer_decode_workspace_bytes(const rt_layer_desc* desc) {
 rt_status rt_layer_decode_step(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past,
                                const void* x_t, void* z_t, void* k_cache, void* v_cache, void* workspace,
                                size_t workspace_bytes, rt_stream_t stream) {
-    RT_TRY(check_layer(desc));
+    RT_TRY(rt::check_decode_args(desc, w, n_past, x_t, z_t, k_cache, v_cache));
     RT_TRY(check_layer_ptrs(w, x_t, z_t, k_cache, v_cache, workspace));
-    if (n_past < 0 || n_past >= desc->attn.seq_len)
-        return fail(RT_ERR_INVALID_ARG, "n_past=%d outside 0..%d (seq_len is the cache capacity)", n_past,
-                    desc->attn.seq_len - 1);
     const size_t need = layout_of(desc, Mode::Decode).total;
     if (workspace_bytes < need)
         return fail(RT_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", workspace_bytes, need);

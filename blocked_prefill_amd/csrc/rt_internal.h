@@ -195,6 +195,12 @@ bool gemm_shape_supported(rt_dtype dt, int64_t M, int N, int K);
 // computed in fp32: fp32 layers store W_out = p ([rows][cols]); bf16 layers
 // store W_out = [bf16(p) | bf16(p - bf16(p))] ([rows][2 cols]), whose sum is
 // p to ~2^-17 relative (read with a_k = cols, K = 2 cols).
+// The calling thread's error text (rt_last_error) set to a + b; returns st.
+rt_status set_error(rt_status st, const char* a, const char* b);
+// The argument checks of rt_layer_decode_step other than its workspace (no HIP call).
+rt_status check_decode_args(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past, const void* x_t,
+                            void* z_t, void* k_cache, void* v_cache);
+
 hipError_t launch_fold_gain(rt_dtype dt, const void* W, const float* g, void* W_out, int64_t rows, int cols,
                             hipStream_t s);
 

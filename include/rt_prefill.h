@@ -326,6 +326,28 @@ rt_status rt_layer_decode_step(const rt_layer_desc* desc, const rt_layer_weights
                                void* workspace, size_t workspace_bytes, rt_stream_t stream);
 
 /*
+ * rt_layer_decode_step_static -- rt_layer_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and kernels, with no
+ * workspace argument. Its scratch is a device array of
+ * RT_DECODE_STATIC_SCRATCH_BYTES inside the library; every GPU that loads the
+ * library holds its own copy until the process ends. The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *   Arguments, layouts and results: as rt_layer_decode_step.
+ *   RT_ERR_WORKSPACE when rt_layer_decode_workspace_bytes(desc) exceeds
+ *   RT_DECODE_STATIC_SCRATCH_BYTES (e.g. B=512, d=1024, F=4096 with RMS
+ *   gains needs ~39 MiB: it fits).
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * contents (nothing in it needs clearing: every byte a call reads, the same
+ * call has written). Calls that overlap in time on one GPU (two streams, two
+ * host threads) race on the array: serialise them.
+ */
+#define RT_DECODE_STATIC_SCRATCH_BYTES (64u << 20)
+rt_status rt_layer_decode_step_static(const rt_layer_desc* desc, const rt_layer_weights* w, int32_t n_past,
+                                      const void* x_t, void* z_t, void* k_cache, void* v_cache,
+                                      rt_stream_t stream);
+
+/*
  * Plans: the same computation as rt_layer_forward, with its O(N) launches
  * recorded once into a HIP graph and replayed by one launch (the paper's
  * section 6.2 records its step loop as a CUDA graph for the same reason).
