@@ -153,6 +153,101 @@ def traffic_summary(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+UPDATE_COUNTER_PASSES = [
+    # one rocprofv3 --pmc pass each over `bench.py --counters` (at most 8 SQ counters per pass)
+    "GRBM_GUI_ACTIVE SQ_WAVE_CYCLES SQ_BUSY_CU_CYCLES SQ_ACTIVE_INST_VALU SQ_VALU_MFMA_BUSY_CYCLES "
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_LDS SQ_INSTS_VALU_TRANS_F32",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD "
+    "SQ_INSTS_VMEM_WR SQ_ACTIVE_INST_VMEM SQ_WAVES TA_BUSY_avr TCP_TCC_READ_REQ_sum TCP_TCC_WRITE_REQ_sum",
+]
+
+
+def counter_summary(dirs):
+    """Per block size b, the update launches of `bench.py --counters` (t = 1..2047 of the
+    stack workload's layer) from the rocprofv3 counter passes of UPDATE_COUNTER_PASSES, one
+    directory per pass: time from the dispatch timestamps, the clock the CUs actually ran at,
+    the vector ALU, matrix core, LDS and memory shares of the SIMDs' cycles, and instruction
+    counts per step. Prints the text kept under profiles/."""
+    import csv
+    N, P = 2048, 512 * 16
+    vals = {}  # (dispatch index among update launches, counter) -> value (one pass per counter)
+    dur = {}   # dispatch index -> durations (ns) over the passes
+    for d in dirs:
+        rows = {}
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            if "update_" not in r["Kernel_Name"]:
+                continue
+            e = rows.setdefault(int(r["Dispatch_Id"]), {})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+            e["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        ids = sorted(rows)[-(N - 1):]  # the last 2047 update launches: the sequence t = 1..2047
+        assert len(ids) == N - 1, (d, len(ids))
+        for i, key in enumerate(ids):
+            for c, v in rows[key].items():
+                if c == "_ns":
+                    dur.setdefault(i, []).append(v)
+                elif (i, c) not in vals:
+                    vals[(i, c)] = v
+    simds = 1024
+    lines = [
+        "# Hardware counters of the blocked-update launches, one layer of the 6-layer stack workload",
+        "# (B=512, N=2048, d_model=1024, 16 heads x 64, bf16): the 2047 launches t = 1..2047, by block size.",
+        "#",
+        "# Commands (repository root, one MI355X; one counter pass each; then the summary):",
+    ]
+    for i, ps in enumerate(UPDATE_COUNTER_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {ps} --output-format csv -d gpurun_out/upc{i} -o run -- "
+                     "python3 bench.py --counters")
+    lines += [
+        "#   python3 bench.py --counter-summary " + " ".join(f"gpurun_out/upc{i}" for i in range(len(dirs))),
+        "# (counter mode serialises the launches: times are those of single dispatches)",
+        "#",
+        "# us/step: End - Start timestamp of the dispatch, mean over the passes.",
+        "# MHz: the clock the CUs ran at, SQ_BUSY_CU_CYCLES / 256 CUs / time (the counter sums the busy",
+        "#   cycles of every CU; GRBM_GUI_ACTIVE / 8 XCDs gives the same within 2% on the large launches,",
+        "#   while on launches of a few us it also counts the counters' own set-up).",
+        "# Shares of the SIMDs' cycles (4 x SQ_BUSY_CU_CYCLES):",
+        "#   valu = SQ_ACTIVE_INST_VALU x 4 (the counter is in units of 4 cycles);",
+        "#   mfma = SQ_VALU_MFMA_BUSY_CYCLES (32 cycles per 32x32x16 bf16 MFMA); coexec = the part of",
+        "#   the mfma cycles during which the SIMD also issued vector ALU work, SQ_VALU_MFMA_COEXEC_CYCLES;",
+        "#   lds = SQ_ACTIVE_INST_LDS x 4; waves = SQ_WAVE_CYCLES x 4 / SIMD cycles (resident waves per",
+        "#   SIMD); wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (resident wave time spent waiting on a memory",
+        "#   or LDS result); ta = TA_BUSY_avr / per-CU cycles (address unit busy).",
+        "# Per step: vector (MFMA included), transcendental (exp2), matrix, LDS, memory-read and -write",
+        "#   instructions (wave level); LDS bank-conflict cycles per LDS instruction; L2 read / write",
+        "#   requests per KB of algorithmic traffic.",
+        "",
+        "| b | steps | us/step | MHz | valu | mfma | coexec | lds | waves | wait | ta | VALU/step | TRANS | MFMA "
+        "| LDS | VMEM rd | VMEM wr | bank confl/LDS inst | L2 rd req/KB | L2 wr req/KB |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    b = 1
+    while b < N:
+        ts = [t for t in range(1, N) if t & -t == b]
+        get = lambda c: sum(vals.get((t - 1, c), 0.0) for t in ts)
+        secs = sum(sum(dur[t - 1]) / len(dur[t - 1]) for t in ts) * 1e-9
+        cu_cyc = max(get("SQ_BUSY_CU_CYCLES"), 1.0)   # summed over the 256 CUs
+        simd_cyc = 4 * cu_cyc
+        byts = sum(update_bytes(t, N, P, 64, 2) for t in ts)
+        n = len(ts)
+        row = [f"{b}", f"{n}", f"{secs / n * 1e6:.1f}", f"{simd_cyc / simds / secs / 1e6:.0f}",
+               f"{get('SQ_ACTIVE_INST_VALU') * 4 / simd_cyc:.2f}", f"{get('SQ_VALU_MFMA_BUSY_CYCLES') / simd_cyc:.2f}",
+               f"{get('SQ_VALU_MFMA_COEXEC_CYCLES') / simd_cyc:.2f}",
+               f"{get('SQ_ACTIVE_INST_LDS') * 4 / simd_cyc:.2f}",
+               f"{get('SQ_WAVE_CYCLES') * 4 / simd_cyc:.2f}",
+               f"{get('SQ_WAIT_INST_ANY') / max(get('SQ_WAVE_CYCLES'), 1):.2f}",
+               f"{get('TA_BUSY_avr') / (cu_cyc / 256):.2f}",
+               f"{get('SQ_INSTS_VALU') / n:.3g}", f"{get('SQ_INSTS_VALU_TRANS_F32') / n:.3g}",
+               f"{get('SQ_INSTS_MFMA') / n:.3g}", f"{get('SQ_INSTS_LDS') / n:.3g}",
+               f"{get('SQ_INSTS_VMEM_RD') / n:.3g}", f"{get('SQ_INSTS_VMEM_WR') / n:.3g}",
+               f"{get('SQ_LDS_BANK_CONFLICT') / max(get('SQ_INSTS_LDS'), 1):.2f}",
+               f"{get('TCP_TCC_READ_REQ_sum') / (byts / 1024):.2f}",
+               f"{get('TCP_TCC_WRITE_REQ_sum') / (byts / 1024):.2f}"]
+        lines.append("| " + " | ".join(row) + " |")
+        b *= 2
+    print("\n".join(lines))
+
+
 def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True, t_range=None):
     """Replay one layer's fused update steps t = 1..N-1 on the workspace's q, k', v' and state
     (offsets as laid out by the library: q, k', v', m, l, o first). With timing_torch, each
@@ -247,11 +342,13 @@ def ceilings(dev):
         for b_ in bufs:
             b_.fill_(7)
         ptr = [b_.data_ptr() for b_ in bufs]
-        for reads in (3, 1):
-            def run(reads=reads):
-                rc = probe.rt_probe_stream(ptr[0], ptr[1], ptr[2], ptr[3], n16, reads, 0, stream.cuda_stream)
-                assert rc == 0, rc
-            stream_gbs[reads] = (reads + 1) * (1 << 30) / timed(run) / 1e9
+        for reads in (3, 1):  # the best of a few grid sizes
+            for blocks in (1024, 2048, 4096, 8192):
+                def run(reads=reads, blocks=blocks):
+                    rc = probe.rt_probe_stream(ptr[0], ptr[1], ptr[2], ptr[3], n16, reads, blocks, stream.cuda_stream)
+                    assert rc == 0, rc
+                gbs = (reads + 1) * (1 << 30) / timed(run) / 1e9
+                stream_gbs[reads] = max(stream_gbs.get(reads, 0.0), gbs)
         del bufs
     k = 8192
     a = torch.randn((k, k), dtype=torch.bfloat16, device=dev)
@@ -612,6 +709,9 @@ def main():
                          "Transformer (log-log slopes)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 counter passes over --counters (no GPU needed)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="summarise the update launches' counter passes (UPDATE_COUNTER_PASSES) over --counters, "
+                         "one rocprofv3 output directory per pass, in order (no GPU needed)")
     ap.add_argument("--backward", action="store_true",
                     help="attention backward of the blocked schedule at B=512, 16x64 heads, N=2048")
     ap.add_argument("--layer-backward", action="store_true",
@@ -627,6 +727,8 @@ def main():
 
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (batch rows are independent; "
               "a multi-GPU run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
