@@ -65,6 +65,22 @@ __device__ __forceinline__ void lds_barrier() {
 // chunk column fall in 16 different 4-bank groups.
 __device__ __forceinline__ int swz(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 
+// Waits until at most n vector-memory loads of this wave are outstanding
+// (loads complete in issue order), leaving the newer ones in flight.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | 0x70 | 0xF00 | ((n >> 4) << 14));
+}
+// Barrier of the direct-to-LDS ring: this wave's LDS reads are complete and no
+// memory access is moved across it by the compiler, while the global->LDS
+// loads in flight into the other stages stay in flight (a release fence on
+// LDS would wait for them too).
+__device__ __forceinline__ void dma_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
 // A small blocked step (blocks of 1, 2 or 4 pairs) run by the workgroup that
 // has just produced the newest key/value row of the block for `rows` batch
 // rows of one head (kvs: row r holds k then v, 64 each, as stored). The same
@@ -162,13 +178,19 @@ __device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16
 // v_mfma_f32_32x32x16_bf16; each wave computes a (BM/WM) x (BN/WN) block.
 // One LDS-only barrier per K tile.
 //
+// PIPE_DMA: the K tiles bypass the registers: each wave's 16-byte loads land
+// in LDS directly (global_load_lds_dwordx4, the 64 lanes' data in 64
+// consecutive slots, which are the same swizzled slots as above), in a ring of
+// D stages; tile kt+D-1 is in flight while tile kt is multiplied, and no
+// VGPRs are spent on staging.
+//
 // KS > 1 splits K inside the workgroup: KS groups of WM*WN waves each run the
 // pipeline above over their own contiguous K range, with their own LDS
 // buffers, and the KS partial tiles are added in LDS before the epilogue. At
 // the per-position shapes (M = batch) this multiplies the waves per tile and
 // divides the serial K-loop length without any cross-workgroup reduction.
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS>
-__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
+__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t bx, const uint32_t by) {
     // MF = 32: v_mfma_f32_32x32x16_bf16 blocks; MF = 16: v_mfma_f32_16x16x32_bf16 blocks
     // (four times as many independent accumulators for the same wave tile).
     static_assert(MF == 32 || MF == 16, "MFMA block");
@@ -186,7 +208,10 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
     static_assert(FM >= 1 && FN >= 1 && A_CH % NTG == 0 && W_CH % NTG == 0, "tile shape");
     static_assert(D >= 2, "prefetch depth");
 
-    __shared__ __attribute__((aligned(16))) char smem_all[KS * 2 * STAGE];
+    constexpr bool DMA = (FLAGS & PIPE_DMA) != 0;
+    constexpr int NBUF = DMA ? D : 2;  // LDS stages per K group
+    static_assert(!DMA || (KS == 1 && D >= 3 && (D - 2) * (LA + LW) < 64), "direct-to-LDS ring");
+    __shared__ __attribute__((aligned(16))) char smem_all[KS * NBUF * STAGE];
     __shared__ float rs[BM];     // row scale (1/rms)
     __shared__ float qsum[(FLAGS & EPI_RMS_PARTS) ? BM * 16 : 1];  // per-quad sums of the RMS partials
     // EPI_UPDATE: the tile's k|v rows as stored (bf16), read by the fused step
@@ -194,11 +219,11 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int grp = tid / NTG, gtid = tid % NTG, wave = gtid >> 6;
-    char* const smem = smem_all + grp * 2 * STAGE;  // this K group's double buffer
+    char* const smem = smem_all + grp * NBUF * STAGE;  // this K group's stage buffers
     const int wm = wave / WN, wn = wave % WN;
     const int gq = lane >> 5;
-    const int64_t m0 = (int64_t)blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    const int64_t m0 = (int64_t)by * BM;
+    const int n0 = bx * BN;
     // PAIRED: tile n holds rows n*BN/2 .. of W[0] (its left half) and of W[1] (its right half)
     constexpr bool PAIRED = (FLAGS & EPI_PAIRKV) != 0;
     constexpr int HB = BN / 2;
@@ -227,7 +252,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
                           : W + (int64_t)r * ldw + c * 8;
     }
 
-    bf16x8 ra[D][LA], rw[D][LW];
+    bf16x8 ra[DMA ? 1 : D][LA], rw[DMA ? 1 : D][LW];
     const int a_k = g.a_k ? g.a_k : g.K;  // A's own columns: column k reads k mod a_k (split weights)
     auto load = [&](int u, int k0) {
         const int ka = k0 >= a_k ? k0 - a_k : k0;
@@ -242,6 +267,21 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
         for (int i = 0; i < LA; ++i) *reinterpret_cast<bf16x8*>(base + a_slot[i] * 16) = ra[u][i];
 #pragma unroll
         for (int i = 0; i < LW; ++i) *reinterpret_cast<bf16x8*>(base + (A_CH + NTG * i + gtid) * 16) = rw[u][i];
+    };
+
+    // PIPE_DMA: K tile k0 into LDS stage buf (a wave's 64 lanes fill 64 consecutive slots)
+    auto dma = [&](int buf, int k0) {
+        const int ka = k0 >= a_k ? k0 - a_k : k0;
+        char* base = smem + buf * STAGE + wave * 64 * 16;
+#pragma unroll
+        for (int i = 0; i < LA; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ka),
+                                             (__attribute__((address_space(3))) void*)(base + NTG * i * 16), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < LW; ++i)
+            __builtin_amdgcn_global_load_lds((const void*)(w_src[i] + k0),
+                                             (__attribute__((address_space(3))) void*)(base + (A_CH + NTG * i) * 16), 16,
+                                             0, 0);
     };
 
     acc_t acc[FM][FN];
@@ -299,11 +339,17 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
     const int KT = g.K / BK / KS;
     const int k_first = grp * KT * BK;
     const int last = k_first + (KT - 1) * BK;
-    // prologue: tiles 0..D-1 in flight, tile 0 in LDS buffer 0, tile D replaces it in the ring
+    if constexpr (DMA) {
+        // prologue: tiles 0..D-2 in flight into stages 0..D-2
 #pragma unroll
-    for (int u = 0; u < D; ++u) load(u, min(k_first + u * BK, last));
-    store(0, 0);
-    load(0, min(k_first + D * BK, last));
+        for (int u = 0; u < D - 1; ++u) dma(u, min(k_first + u * BK, last));
+    } else {
+        // prologue: tiles 0..D-1 in flight, tile 0 in LDS buffer 0, tile D replaces it in the ring
+#pragma unroll
+        for (int u = 0; u < D; ++u) load(u, min(k_first + u * BK, last));
+        store(0, 0);
+        load(0, min(k_first + D * BK, last));
+    }
     // partial sums of squares of this tile's A rows (EPI_RMS_PARTS), laid out
     // [M][n_parts] with n_parts % 4 == 0 and <= 64: fetched as float4s behind
     // the first K tiles (so the main loop's first waits do not include them),
@@ -359,15 +405,35 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
             }
     }
 
-    for (int kt0 = 0; kt0 < KT; kt0 += D) {
+    if constexpr (DMA) {
+        // iteration kt: this wave's loads of tile kt are complete once at most
+        // the D-2 newer tiles' loads are outstanding (the row-sum and residual
+        // loads above only make the first waits longer); the barrier then makes
+        // every wave's part visible and frees stage (kt-1)%D, which takes tile
+        // kt+D-1. Prefetches past the last tile reload it into stages nobody
+        // reads again; they have landed before the epilogue reuses the stages.
+        for (int kt0 = 0; kt0 < KT; kt0 += D) {
 #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            const int kt = kt0 + u;
-            lds_barrier();                 // tile kt is in LDS; tile kt-1's buffer is free
-            compute(kt & 1);
-            const int nu = (u + 1) % D;    // ring stage of tile kt+1 (constant once unrolled)
-            store(nu, (kt + 1) & 1);
-            load(nu, min(k_first + (kt + 1 + D) * BK, last));
+            for (int u = 0; u < D; ++u) {
+                const int kt = kt0 + u;
+                wait_vm<(D - 2) * (LA + LW)>();
+                dma_barrier();
+                dma((u + D - 1) % D, min(k_first + (kt + D - 1) * BK, last));
+                compute(u);
+            }
+        }
+        wait_vm<0>();
+    } else {
+        for (int kt0 = 0; kt0 < KT; kt0 += D) {
+#pragma unroll
+            for (int u = 0; u < D; ++u) {
+                const int kt = kt0 + u;
+                lds_barrier();                 // tile kt is in LDS; tile kt-1's buffer is free
+                compute(kt & 1);
+                const int nu = (u + 1) % D;    // ring stage of tile kt+1 (constant once unrolled)
+                store(nu, (kt + 1) & 1);
+                load(nu, min(k_first + (kt + 1 + D) * BK, last));
+            }
         }
     }
 
@@ -435,7 +501,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
         float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kg = 0; kg < KS; ++kg) {
-            const float* t = tl0 + kg * (2 * STAGE / 4) + rl * LDT + c0;
+            const float* t = tl0 + kg * (NBUF * STAGE / 4) + rl * LDT + c0;
             const float4 p0 = *reinterpret_cast<const float4*>(t);
             const float4 p1 = *reinterpret_cast<const float4*>(t + 4);
             v[0] += p0.x; v[1] += p0.y; v[2] += p0.z; v[3] += p0.w;
@@ -528,7 +594,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g) {
 
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
 __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_kernel(GemmArgs g) {
-    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g);
+    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g, blockIdx.x, blockIdx.y);
 }
 
 // Several products of the same kind and shape in one launch (blockIdx.z picks
@@ -542,9 +608,19 @@ static_assert(sizeof(GemmGroup) <= 3584, "kernel argument size");
 
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS = 1>
 __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_group_kernel(GemmGroup gg) {
-    const GemmArgs& g = gg.g[blockIdx.z];
-    if ((int64_t)blockIdx.y * BM >= g.M) return;  // past this product's rows (the whole workgroup)
-    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g);
+    uint32_t bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+    if constexpr ((FLAGS & PIPE_XCD) != 0) {
+        // workgroup i runs on XCD i % 8: give XCD x the x-th eighth of the (z, y, x) tiles
+        const uint32_t gxy = gridDim.x * gridDim.y, nwg = gxy * gridDim.z;
+        uint32_t lin = bx + gridDim.x * (by + gridDim.y * bz);
+        if ((nwg & 7) == 0) lin = (lin & 7) * (nwg >> 3) + (lin >> 3);
+        bz = lin / gxy;
+        by = (lin % gxy) / gridDim.x;
+        bx = lin % gridDim.x;
+    }
+    const GemmArgs& g = gg.g[bz];
+    if ((int64_t)by * BM >= g.M) return;  // past this product's rows (the whole workgroup)
+    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g, bx, by);
 }
 
 // The products of one launch: n argument sets of one kind and shape (n <= kMaxGemmGroup).
@@ -668,7 +744,13 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
-                if (grouped) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, 2, 16>(gs, s);
+                if (grouped) {
+                    // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 17.4 us against 19.3
+                    if constexpr (D == 4)
+                        return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS | PIPE_DMA | PIPE_XCD, 64, 64, 2, 2, 4,
+                                        16>(gs, s);
+                    return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 64, 64, 2, 2, 2, 16>(gs, s);
+                }
             }
             if constexpr (KS <= 2)
                 if (!big)  // 2x2 waves per K group (6.6 us against 7.0 for 2x1, M = 512)
@@ -692,7 +774,14 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if constexpr (KS == 1) {
                 if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
-                if (grouped) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 4, 2, 32>(gs, s);
+                if (grouped) {
+                    // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 40.4-40.8 us against
+                    // 44.9-45.1 (the weight and A fetches from outside L2 halve: 66 MB against 126)
+                    if constexpr (D == 4)
+                        return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS | PIPE_DMA | PIPE_XCD, 128, 128, 2, 4, 4, 32>(
+                            gs, s);
+                    return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 4, 2, 32>(gs, s);
+                }
             }
             if (!big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 64, kRowSSTile, 2, 1, D, 16, KS>(gs, s);
             break;

@@ -90,6 +90,12 @@ enum : int {
     EPI_UPDATE = 256,   // (with EPI_PAIRKV, bf16, head_dim 64) then run upd, a small blocked step whose
                         // newest key/value row is this product's output (see gemm.hip)
     EPI_DGELU = 512,    // multiply by GELU'(R[row][col]) (the backward through the MLP's activation)
+    // kernel shape (not epilogue) flags, bf16 pipelined kernel:
+    PIPE_DMA = 1024,    // K tiles go straight from global memory into a ring of D LDS stages
+                        // (global_load_lds), no register staging; one K group
+    PIPE_XCD = 2048,    // grouped launch: the workgroups an XCD runs take one contiguous range of
+                        // (product, row tile, column tile), so a weight slab and an A row block are
+                        // each fetched into few XCDs' L2
 };
 struct GemmArgs {
     const void* A;      // [M][lda]
