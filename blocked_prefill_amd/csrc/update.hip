@@ -278,8 +278,13 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
     constexpr int KSTR = DH + 8;    // bf16 per K row in LDS (16-byte pad)
     constexpr int VSTR = KT + 8;    // bf16 per V^T row in LDS
     constexpr int NT = 64 * WAVES;
-    __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KSTR];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[DH * VSTR];
+    // K and V^T tiles; after the key loop the same bytes hold each wave's
+    // 32 x 32 fp32 transpose tile of the state rows (pitch TP floats)
+    constexpr int TP = 36;
+    constexpr int LDS_KV = (KT * KSTR + DH * VSTR) * 2, LDS_T = WAVES * 32 * TP * 4;
+    __shared__ __attribute__((aligned(16))) char lds_raw[LDS_KV > LDS_T ? LDS_KV : LDS_T];
+    bf16* const Ks = reinterpret_cast<bf16*>(lds_raw);
+    bf16* const Vt = Ks + KT * KSTR;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, ql = lane & 31;
@@ -484,10 +489,10 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
         }
     }
     l_run += __shfl_xor(l_run, 32, 64);  // the two halves of each query's row sum
-    if (!qvalid) return;
 
     // this lane holds dh = blk*32 + 8*ee + 4*g + (0..3) for blk in {0,1}, ee in 0..3 (accumulator e = 4*ee + i)
     if constexpr (CAUSAL) {
+        if (!qvalid) return;
         const float inv = 1.0f / l_run;
         bf16* out = (bf16*)a.a_out + j * slab + pair * DH;
 #pragma unroll
@@ -503,14 +508,22 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
         }
         return;
     }
+    // Merge with the stored state: new = stored * cs + this block's * cb.
     const int64_t sidx = j * a.P + pair;
-    float* orow = a.o + sidx * DH;
-    if (!a.init) {
+    const bool fin_row = a.fin && qrow == 0;
+    float cs = 0.f, cb = 1.f;
+    if (!a.init && qvalid) {
         const float ms = a.m[sidx], ls = a.l[sidx];
         const float m_new = fmaxf(ms, m_run);
-        const float cs = fast_exp2(ms - m_new), cb = fast_exp2(m_run - m_new);
+        cs = fast_exp2(ms - m_new);
+        cb = fast_exp2(m_run - m_new);
         l_run = ls * cs + l_run * cb;
         m_run = m_new;
+    }
+    // the stored numerator of the finishing row (the only one the registers merge
+    // when the rows go through LDS below), or of every row of this lane
+    auto merge_regs = [&]() {
+        const float* orow = a.o + sidx * DH;
 #pragma unroll
         for (int ee = 0; ee < 4; ++ee) {
             const float4 s0 = *reinterpret_cast<const float4*>(orow + 8 * ee + 4 * g);
@@ -524,8 +537,64 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
             o1[4 * ee + 2] = s1.z * cs + o1[4 * ee + 2] * cb;
             o1[4 * ee + 3] = s1.w * cs + o1[4 * ee + 3] * cb;
         }
+    };
+    if (qvalid && !fin_row && g == 0) {
+        a.m[sidx] = m_run;
+        a.l[sidx] = l_run;
     }
-    if (a.fin && qrow == 0) {
+    if constexpr (WAVES <= 2) {
+        // One or two waves per workgroup (blocks of 32 and 64 pairs, where the
+        // state is half the step's bytes): the fp32 numerator rows (256 bytes per
+        // query) go through LDS so that they are read and written as whole
+        // 128-byte lines. Each wave writes its O^T, 32 dh at a time, transposed
+        // into its tile; then each 8 lanes move one query's 32 values
+        // (b = 64: 114 us per step against 126 with a lane's 16-byte pieces of
+        // 32 rows; with four waves the extra pass cost more than it saved).
+        lds_fence_barrier();  // every wave is done with the K/V tiles
+        float* tw = reinterpret_cast<float*>(lds_raw) + wave * 32 * TP;
+        if (g == 0) tw[ql * TP + 32] = cs;  // each query's cs, in the tile's padding column
+        const int rr = lane >> 3, cc = (lane & 7) * 4;  // this lane's row (of 8 per pass) and 4 columns
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            // lane (ql, g) holds dh = blk*32 + 8*ee + 4*g + i of query ql
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee)
+                *reinterpret_cast<float4*>(&tw[ql * TP + 8 * ee + 4 * g]) =
+                    blk ? make_float4(o1[4 * ee] * cb, o1[4 * ee + 1] * cb, o1[4 * ee + 2] * cb, o1[4 * ee + 3] * cb)
+                        : make_float4(o0[4 * ee] * cb, o0[4 * ee + 1] * cb, o0[4 * ee + 2] * cb, o0[4 * ee + 3] * cb);
+#pragma unroll
+            for (int pass = 0; pass < 4; ++pass) {
+                const int r = pass * 8 + rr, row = wave_q0 + r;
+                float4 v = *reinterpret_cast<const float4*>(&tw[r * TP + cc]);
+                if (row < a.nq && !(a.fin && row == 0)) {
+                    float* op = a.o + ((int64_t)(a.q0 + row) * a.P + pair) * DH + blk * 32 + cc;
+                    if (!a.init) {
+                        const float c = tw[r * TP + 32];
+                        const float4 sv = *reinterpret_cast<const float4*>(op);
+                        v = make_float4(sv.x * c + v.x, sv.y * c + v.y, sv.z * c + v.z, sv.w * c + v.w);
+                    }
+                    *reinterpret_cast<float4*>(op) = v;
+                }
+            }
+        }
+        if (!fin_row || !qvalid) return;
+        if (!a.init) merge_regs();
+    } else {
+        if (!qvalid) return;
+        if (!a.init) merge_regs();
+        if (!fin_row) {
+            float* orow = a.o + sidx * DH;
+#pragma unroll
+            for (int ee = 0; ee < 4; ++ee) {
+                *reinterpret_cast<float4*>(orow + 8 * ee + 4 * g) =
+                    make_float4(o0[4 * ee + 0], o0[4 * ee + 1], o0[4 * ee + 2], o0[4 * ee + 3]);
+                *reinterpret_cast<float4*>(orow + 32 + 8 * ee + 4 * g) =
+                    make_float4(o1[4 * ee + 0], o1[4 * ee + 1], o1[4 * ee + 2], o1[4 * ee + 3]);
+            }
+            return;
+        }
+    }
+    {
         // the position's own ephemeral pair (lanes 0 and 32 hold the two halves of the query)
         const bf16* kp = (const bf16*)a.k_eph + j * slab + pair * DH + 8 * g;
         float d = 0.f;
@@ -557,18 +626,6 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
                 }
                 *reinterpret_cast<bf16x4*>(out + dh0) = r;
             }
-        }
-    } else {
-        if (g == 0) {
-            a.m[sidx] = m_run;
-            a.l[sidx] = l_run;
-        }
-#pragma unroll
-        for (int ee = 0; ee < 4; ++ee) {
-            *reinterpret_cast<float4*>(orow + 8 * ee + 4 * g) =
-                make_float4(o0[4 * ee + 0], o0[4 * ee + 1], o0[4 * ee + 2], o0[4 * ee + 3]);
-            *reinterpret_cast<float4*>(orow + 32 + 8 * ee + 4 * g) =
-                make_float4(o1[4 * ee + 0], o1[4 * ee + 1], o1[4 * ee + 2], o1[4 * ee + 3]);
         }
     }
 }
