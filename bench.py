@@ -248,6 +248,68 @@ def counter_summary(dirs):
     print("\n".join(lines))
 
 
+FAMILY_COUNTERS = ("GRBM_GUI_ACTIVE SQ_BUSY_CU_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES "
+                   "SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_MFMA SQ_INSTS_VALU")
+
+
+def _kernel_family(name, grid):
+    """A short label for a kernel of the stack (template arguments: FLAGS first for the GEMMs)."""
+    import re
+    m = re.search(r"<([^<>]*)>\(", name)
+    args = [a.strip() for a in m.group(1).split(",")] if m else re.findall(r"Li(\d+)E", name)
+    ints = [int(a) for a in args if a.lstrip("-").isdigit()]
+    if "gemm_pipe" in name and ints:
+        flags, shape = ints[0], "x".join(str(v) for v in ints[1:3])
+        kind = {20: "W_2", 10: "W_1", 8: "W_kv or QKV", 52: "W_o", 392: "W_kv + small step",
+                24: "W_2", 40: "W_o"}.get(flags & 1023, f"flags {flags & 1023}")
+        how = ("grouped " if "group" in name else "") + kind + f" {shape}"
+        if flags & 1024:
+            how += ", K tiles to LDS directly"
+        if flags & 2048:
+            how += ", XCD-grouped"
+        return how
+    for k in ("update_small_group", "update_small", "update_simt", "update_mfma_multi", "update_mfma", "row_sumsq"):
+        if k in name:
+            return k + (f"<{','.join(str(v) for v in ints[:2])}>" if k == "update_mfma" else "")
+    return name[:60]
+
+
+def family_summary(dirs):
+    """MFMA and vector-ALU shares per kernel family of one eager stack forward, from one rocprofv3
+    pass of FAMILY_COUNTERS over `bench.py --eager --steps 1 --warmup 0 --no-cpu --no-kernel-timing`.
+    Time from the dispatch timestamps; SIMD cycles = 4 x SQ_BUSY_CU_CYCLES (the busy cycles of
+    the CUs that had work, at the clock they ran at)."""
+    import collections
+    import csv
+    fam = collections.defaultdict(lambda: collections.defaultdict(float))
+    seen = set()
+    for d in dirs:
+        for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+            name = r["Kernel_Name"]
+            if "rt::" not in name and "_ZN2rt" not in name:
+                continue
+            f = fam[_kernel_family(name, int(r["Grid_Size"]))]
+            f[r["Counter_Name"]] += float(r["Counter_Value"])
+            key = (d, r["Dispatch_Id"])
+            if key not in seen:
+                seen.add(key)
+                f["_n"] += 1
+                f["_ns"] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    lines = [
+        "| family | dispatches | ms | MHz | MFMA busy | VALU busy | waves/SIMD | wait any | wait LDS |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+    for name, f in sorted(fam.items(), key=lambda kv: -kv[1]["_ns"]):
+        cu = max(f["SQ_BUSY_CU_CYCLES"], 1.0)
+        simd = 4 * cu
+        secs = f["_ns"] * 1e-9
+        wc = max(f["SQ_WAVE_CYCLES"], 1.0)
+        lines.append(f"| {name} | {f['_n']:.0f} | {secs * 1e3:.2f} | {cu / 256 / max(secs, 1e-12) / 1e6:.0f} | "
+                     f"{f['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.3f} | {f['SQ_ACTIVE_INST_VALU'] * 4 / simd:.3f} | "
+                     f"{wc * 4 / simd:.2f} | {f['SQ_WAIT_INST_ANY'] / wc:.2f} | {f['SQ_WAIT_INST_LDS'] / wc:.2f} |")
+    print("\n".join(lines))
+
+
 def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True, t_range=None):
     """Replay one layer's fused update steps t = 1..N-1 on the workspace's q, k', v' and state
     (offsets as laid out by the library: q, k', v', m, l, o first). With timing_torch, each
@@ -688,6 +750,48 @@ def decode(args):
                       "hbm_floor_ms": round(floor_ms, 4), "frac_of_floor": round(floor_ms / ms, 4)}))
 
 
+def vendor_gemm():
+    """torch's bf16 products (the vendor GEMM library) on the shapes of the 6-layer stack's
+    products: six per-position products of 512 rows in one batched call (the grouped launch),
+    one of them alone, and a 65536-row chunk of the up-front q|k'|v' projection. Plain products,
+    no fused normalisation, activation or residual; operands contiguous, weights pre-transposed."""
+    import torch
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rnd = lambda *s: torch.randn(*s, device=dev, generator=g).to(torch.bfloat16).contiguous()
+
+    def timed(f, n):
+        for _ in range(5):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    rows = []
+    for name, (m, n, k) in (("W_o", (512, 1024, 1024)), ("W_1", (512, 4096, 1024)), ("W_2", (512, 1024, 4096)),
+                            ("W_kv", (512, 2048, 1024))):
+        a, b = rnd(6, m, k), rnd(6, k, n)
+        us = timed(lambda: torch.bmm(a, b), 50)
+        rows.append({"product": f"{name} x6", "shape": f"6 x [{m}x{k}] x [{k}x{n}]", "us": round(us, 2),
+                     "TFLOP_s": round(2.0 * 6 * m * n * k / us * 1e-6, 1)})
+        a1, b1 = rnd(m, k), rnd(k, n)
+        us = timed(lambda: torch.mm(a1, b1), 50)
+        rows.append({"product": f"{name} x1", "shape": f"[{m}x{k}] x [{k}x{n}]", "us": round(us, 2),
+                     "TFLOP_s": round(2.0 * m * n * k / us * 1e-6, 1)})
+    a, b = rnd(65536, 1024), rnd(1024, 3072)
+    us = timed(lambda: torch.mm(a, b), 20)
+    rows.append({"product": "q|k'|v' chunk", "shape": "[65536x1024] x [1024x3072]", "us": round(us, 2),
+                 "TFLOP_s": round(2.0 * 65536 * 1024 * 3072 / us * 1e-6, 1)})
+    for r in rows:
+        print(json.dumps(r))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -723,12 +827,20 @@ def main():
                     help="run the stack as one graph per layer, one after another (no layer wavefront)")
     ap.add_argument("--decode", action="store_true",
                     help="one decode step of the B=512, d=1024 layer against a 2048-position cache")
+    ap.add_argument("--family-summary", nargs="+", metavar="DIR",
+                    help="MFMA / vector-ALU shares per kernel family from a rocprofv3 pass of FAMILY_COUNTERS "
+                         "over --eager (no GPU needed)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="the vendor library (torch bf16 bmm / mm) on the stack's product shapes, for comparison "
+                         "with this library's kernels in the stack's kernel trace")
     args = ap.parse_args()
 
     if args.traffic_summary:
         return traffic_summary(*args.traffic_summary)
     if args.counter_summary:
         return counter_summary(args.counter_summary)
+    if args.family_summary:
+        return family_summary(args.family_summary)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (batch rows are independent; "
               "a multi-GPU run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
@@ -745,6 +857,8 @@ def main():
         build.build()
     rt.load()
 
+    if args.vendor_gemm:
+        return vendor_gemm()
     if args.sweep:
         return sweep(args)
     if args.decode:
