@@ -310,6 +310,51 @@ def family_summary(dirs):
     print("\n".join(lines))
 
 
+def trace_summary(d, replays):
+    """Tables from a rocprofv3 --kernel-trace --stats run of the stack bench (`replays` plan replays:
+    warm-up + timed steps): kernels by total time, and per family the launches inside the plan
+    replays, per replay, with the average of the grouped products' six-layer launches (grid z = 6)."""
+    import collections
+    import csv
+    import gzip
+    rows = list(csv.DictReader(open(os.path.join(d, "run_kernel_stats.csv"))))
+    out = ["| kernel (family) | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
+    for r in rows[:16]:
+        out.append(f"| {_kernel_family(r['Name'], 0)} | {r['Calls']} | {int(r['TotalDurationNs']) / 1e6:.2f} | "
+                   f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    tp = os.path.join(d, "run_kernel_trace.csv")
+    f = gzip.open(tp + ".gz", "rt") if os.path.exists(tp + ".gz") else open(tp)
+    tr = [r for r in csv.DictReader(f) if "rt::" in r["Kernel_Name"] or "_ZN2rt" in r["Kernel_Name"]]
+    # the replays' window: from layer 0's row sums of all N*B rows (a replay's first launch)
+    # to the end of the last product
+    first = [int(r["Start_Timestamp"]) for r in tr
+             if "row_sumsq" in r["Kernel_Name"] and int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) >= 1 << 26]
+    ends = [int(r["End_Timestamp"]) for r in tr if "gemm_pipe" in r["Kernel_Name"]]
+    if first and ends:
+        lo, hi = min(first), max(ends)
+        fam = collections.defaultdict(lambda: [0, 0.0, 0, 0.0])
+        t0, t1 = None, None
+        for r in tr:
+            st, en = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            if st < lo or st > hi:
+                continue
+            t0 = st if t0 is None else min(t0, st)
+            t1 = en if t1 is None else max(t1, en)
+            e = fam[_kernel_family(r["Kernel_Name"], 0)]
+            e[0] += 1
+            e[1] += (en - st) * 1e-3
+            if int(r["Grid_Size_Z"]) == 6:
+                e[2] += 1
+                e[3] += (en - st) * 1e-3
+        out += ["", f"Inside the {replays} plan replays ({(t1 - t0) / 1e6:.1f} ms from the first launch to the last product), "
+                    "per replay:", "",
+                "| family | launches | ms | avg us | six-layer launches | their avg us |", "|---|---|---|---|---|---|"]
+        for k, (n, us, n6, us6) in sorted(fam.items(), key=lambda kv: -kv[1][1]):
+            out.append(f"| {k} | {n // replays} | {us / 1e3 / replays:.2f} | {us / n:.2f} | {n6 // replays} | "
+                       f"{(us6 / n6) if n6 else float('nan'):.2f} |")
+    print("\n".join(out))
+
+
 def update_sequence(rt, attn, ws, k_cache, v_cache, N, B, H, D, stream, timing_torch, sync=True, t_range=None):
     """Replay one layer's fused update steps t = 1..N-1 on the workspace's q, k', v' and state
     (offsets as laid out by the library: q, k', v', m, l, o first). With timing_torch, each
@@ -754,7 +799,8 @@ def vendor_gemm():
     """torch's bf16 products (the vendor GEMM library) on the shapes of the 6-layer stack's
     products: six per-position products of 512 rows in one batched call (the grouped launch),
     one of them alone, and a 65536-row chunk of the up-front q|k'|v' projection. Plain products,
-    no fused normalisation, activation or residual; operands contiguous, weights pre-transposed."""
+    no fused normalisation, activation or residual; operands contiguous, weights pre-transposed.
+    Timed as graph replays of back-to-back launches (the kernels' time, not the host's launch rate)."""
     import torch
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev)
@@ -762,16 +808,26 @@ def vendor_gemm():
     rnd = lambda *s: torch.randn(*s, device=dev, generator=g).to(torch.bfloat16).contiguous()
 
     def timed(f, n):
-        for _ in range(5):
-            f()
+        # n launches captured in one graph, so that the host's launch rate does not set the time
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                f()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            for _ in range(n):
+                f()
+        graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
         e0.record()
-        for _ in range(n):
-            f()
+        for _ in range(reps):
+            graph.replay()
         e1.record()
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
+        return e0.elapsed_time(e1) * 1e3 / (n * reps)
 
     rows = []
     for name, (m, n, k) in (("W_o", (512, 1024, 1024)), ("W_1", (512, 4096, 1024)), ("W_2", (512, 1024, 4096)),
@@ -830,6 +886,8 @@ def main():
     ap.add_argument("--family-summary", nargs="+", metavar="DIR",
                     help="MFMA / vector-ALU shares per kernel family from a rocprofv3 pass of FAMILY_COUNTERS "
                          "over --eager (no GPU needed)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DIR", "REPLAYS"),
+                    help="tables from a rocprofv3 --kernel-trace --stats run of the stack bench (no GPU needed)")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="the vendor library (torch bf16 bmm / mm) on the stack's product shapes, for comparison "
                          "with this library's kernels in the stack's kernel trace")
@@ -841,6 +899,8 @@ def main():
         return counter_summary(args.counter_summary)
     if args.family_summary:
         return family_summary(args.family_summary)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary[0], int(args.trace_summary[1]))
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (batch rows are independent; "
               "a multi-GPU run would shard the batch with no exchange). Run with --gpus 1.", file=sys.stderr)
