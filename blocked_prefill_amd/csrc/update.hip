@@ -271,7 +271,8 @@ __device__ __forceinline__ void lds_fence_barrier() {
 // queries' own positions (kv0 = q0 = 0); query i takes key rows 0..i and is
 // written to row i of a_out; no state is read or written.
 template <int WAVES, int KT, bool RAGGED, bool CAUSAL>
-__global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in, int nqt) {
+// (four waves: at most 128 VGPRs, so that four waves share a SIMD)
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 4 : 1)) void update_mfma_kernel(UpdateArgs a_in, int nqt) {
     const UpdateArgs a = level_step(a_in, blockIdx.y);
     if (a.nq <= 0) return;  // the whole workgroup
     constexpr int DH = 64;
@@ -520,8 +521,7 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
         l_run = ls * cs + l_run * cb;
         m_run = m_new;
     }
-    // the stored numerator of the finishing row (the only one the registers merge
-    // when the rows go through LDS below), or of every row of this lane
+    // the stored numerator of the finishing row (the only row merged in registers)
     auto merge_regs = [&]() {
         const float* orow = a.o + sidx * DH;
 #pragma unroll
@@ -542,14 +542,13 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
         a.m[sidx] = m_run;
         a.l[sidx] = l_run;
     }
-    if constexpr (WAVES <= 2) {
-        // One or two waves per workgroup (blocks of 32 and 64 pairs, where the
-        // state is half the step's bytes): the fp32 numerator rows (256 bytes per
-        // query) go through LDS so that they are read and written as whole
+    {
+        // The fp32 numerator rows (256 bytes per query, about half of a step's
+        // bytes) go through LDS so that they are read and written as whole
         // 128-byte lines. Each wave writes its O^T, 32 dh at a time, transposed
-        // into its tile; then each 8 lanes move one query's 32 values
-        // (b = 64: 114 us per step against 126 with a lane's 16-byte pieces of
-        // 32 rows; with four waves the extra pass cost more than it saved).
+        // into its tile; then each 8 lanes move one query's 32 values (b = 64
+        // 128.7 -> 116.3 us per step, b = 128 247 -> 221, b = 256 491 -> 453,
+        // against each lane's 16-byte pieces of 32 rows).
         lds_fence_barrier();  // every wave is done with the K/V tiles
         float* tw = reinterpret_cast<float*>(lds_raw) + wave * 32 * TP;
         if (g == 0) tw[ql * TP + 32] = cs;  // each query's cs, in the tile's padding column
@@ -579,20 +578,6 @@ __global__ __launch_bounds__(64 * WAVES) void update_mfma_kernel(UpdateArgs a_in
         }
         if (!fin_row || !qvalid) return;
         if (!a.init) merge_regs();
-    } else {
-        if (!qvalid) return;
-        if (!a.init) merge_regs();
-        if (!fin_row) {
-            float* orow = a.o + sidx * DH;
-#pragma unroll
-            for (int ee = 0; ee < 4; ++ee) {
-                *reinterpret_cast<float4*>(orow + 8 * ee + 4 * g) =
-                    make_float4(o0[4 * ee + 0], o0[4 * ee + 1], o0[4 * ee + 2], o0[4 * ee + 3]);
-                *reinterpret_cast<float4*>(orow + 32 + 8 * ee + 4 * g) =
-                    make_float4(o1[4 * ee + 0], o1[4 * ee + 1], o1[4 * ee + 2], o1[4 * ee + 3]);
-            }
-            return;
-        }
     }
     {
         // the position's own ephemeral pair (lanes 0 and 32 hold the two halves of the query)
