@@ -182,7 +182,9 @@ __device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16
 // in LDS directly (global_load_lds_dwordx4, the 64 lanes' data in 64
 // consecutive slots, which are the same swizzled slots as above), in a ring of
 // D stages; tile kt+D-1 is in flight while tile kt is multiplied, and no
-// VGPRs are spent on staging.
+// VGPRs are spent on staging. Each stage is an array of its own: the compiler
+// tracks LDS written by these loads per object, and with one array it would
+// wait for every load in flight before each LDS read of the tile.
 //
 // KS > 1 splits K inside the workgroup: KS groups of WM*WN waves each run the
 // pipeline above over their own contiguous K range, with their own LDS
@@ -211,7 +213,18 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     constexpr bool DMA = (FLAGS & PIPE_DMA) != 0;
     constexpr int NBUF = DMA ? D : 2;  // LDS stages per K group
     static_assert(!DMA || (KS == 1 && D >= 3 && (D - 2) * (LA + LW) < 64), "direct-to-LDS ring");
-    __shared__ __attribute__((aligned(16))) char smem_all[KS * NBUF * STAGE];
+    __shared__ __attribute__((aligned(16))) char smem_all[DMA ? 16 : KS * NBUF * STAGE];
+    // PIPE_DMA: each stage its own array, so that the compiler sees a stage's LDS reads and
+    // another stage's global->LDS loads as distinct objects and waits for neither
+    // the epilogue's fp32 tile passes use stage 0 alone: the largest pass of BM, BM/2 or BM/4
+    // rows that fits in a quarter more than a stage sizes it
+    constexpr int EPI_ROW = (BN + 4) * 4;
+    constexpr int EPI_PR = BM * EPI_ROW <= STAGE * 5 / 4 ? BM : BM / 2 * EPI_ROW <= STAGE * 5 / 4 ? BM / 2 : BM / 4;
+    constexpr int STG0 = EPI_PR * EPI_ROW > STAGE ? EPI_PR * EPI_ROW : STAGE;
+    __shared__ __attribute__((aligned(16))) char stg0[DMA ? STG0 : 16];
+    __shared__ __attribute__((aligned(16))) char stg1[DMA ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char stg2[DMA && NBUF > 2 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) char stg3[DMA && NBUF > 3 ? STAGE : 16];
     __shared__ float rs[BM];     // row scale (1/rms)
     __shared__ float qsum[(FLAGS & EPI_RMS_PARTS) ? BM * 16 : 1];  // per-quad sums of the RMS partials
     // EPI_UPDATE: the tile's k|v rows as stored (bf16), read by the fused step
@@ -219,7 +232,11 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int grp = tid / NTG, gtid = tid % NTG, wave = gtid >> 6;
-    char* const smem = smem_all + grp * NBUF * STAGE;  // this K group's stage buffers
+    char* const smem = KS == 1 ? smem_all : smem_all + grp * NBUF * STAGE;  // this K group's stage buffers
+    auto stage_ptr = [&](int b) -> char* {
+        if constexpr (DMA) return b == 0 ? stg0 : b == 1 ? stg1 : b == 2 ? stg2 : stg3;
+        else return smem + b * STAGE;
+    };
     const int wm = wave / WN, wn = wave % WN;
     const int gq = lane >> 5;
     const int64_t m0 = (int64_t)by * BM;
@@ -272,7 +289,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     // PIPE_DMA: K tile k0 into LDS stage buf (a wave's 64 lanes fill 64 consecutive slots)
     auto dma = [&](int buf, int k0) {
         const int ka = k0 >= a_k ? k0 - a_k : k0;
-        char* base = smem + buf * STAGE + wave * 64 * 16;
+        char* base = stage_ptr(buf) + wave * 64 * 16;
 #pragma unroll
         for (int i = 0; i < LA; ++i)
             __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ka),
@@ -298,7 +315,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     // operand fetch: lane holds 8 consecutive k of row (lane % MF), k-group lane / MF
     const int lrow = lane % MF, lgrp = lane / MF;
     auto compute = [&](int buf) {
-        const char* sA = smem + buf * STAGE;
+        const char* sA = stage_ptr(buf);
         const char* sW = sA + A_CH * 16;
         constexpr int KM = MF == 32 ? 16 : 32;  // k per MFMA
         constexpr int GPS = KM / 8;             // 16-byte chunks per MFMA k-slice
@@ -372,8 +389,9 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
     // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes, 256 rows four);
     // each K group stages its partial tile in its own buffers
-    constexpr int PR = (BM * LDT * 4 <= 2 * STAGE) ? BM : (BM / 2 * LDT * 4 <= 2 * STAGE) ? BM / 2 : BM / 4;
-    static_assert(PR * LDT * 4 <= 2 * STAGE && BM % PR == 0, "fp32 tile passes fit the stage buffers");
+    constexpr int EPI_BYTES = DMA ? STG0 : 2 * STAGE;  // LDS the epilogue's fp32 tile passes may use
+    constexpr int PR = (BM * LDT * 4 <= EPI_BYTES) ? BM : (BM / 2 * LDT * 4 <= EPI_BYTES) ? BM / 2 : (BM / 4 * LDT * 4 <= EPI_BYTES) ? BM / 4 : BM / 8;
+    static_assert(PR * LDT * 4 <= EPI_BYTES && BM % PR == 0, "fp32 tile passes fit the stage buffers");
     constexpr int CPRW = BN / 8;               // 8-column runs per row
     constexpr int RUNS = (PR * CPRW + NT - 1) / NT;  // runs per thread per pass
     // The epilogue's run of a thread: (pass, it) -> tile row rl of the pass and
@@ -468,8 +486,8 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     // 4-lane shuffle.
     static_assert(NT % CPRW == 0 && CPRW % 4 == 0, "runs map onto lanes evenly");
     static_assert(!(FLAGS & EPI_ROWSS) || (BN % kRowSSTile == 0 && CPRW >= 4), "32-column groups");
-    float* tl = reinterpret_cast<float*>(smem);          // this group's partial tile
-    const float* tl0 = reinterpret_cast<const float*>(smem_all);
+    float* tl = reinterpret_cast<float*>(DMA ? stg0 : smem);          // this group's partial tile
+    const float* tl0 = reinterpret_cast<const float*>(DMA ? stg0 : smem_all);
     TC* C = (TC*)g.C[seg];
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
