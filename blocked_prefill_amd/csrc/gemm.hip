@@ -387,8 +387,9 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     }
 
     constexpr int LDT = BN + 4;  // fp32 row pitch in LDS
-    // rows per pass through the stage buffers (a 128-row fp32 tile takes two passes, 256 rows four);
-    // each K group stages its partial tile in its own buffers
+    // rows per pass through the stage buffers (register staging: both stages, so a 128-row fp32
+    // tile takes two passes, 256 rows four; PIPE_DMA: stage 0 alone); each K group stages its
+    // partial tile in its own buffers
     constexpr int EPI_BYTES = DMA ? STG0 : 2 * STAGE;  // LDS the epilogue's fp32 tile passes may use
     constexpr int PR = (BM * LDT * 4 <= EPI_BYTES) ? BM : (BM / 2 * LDT * 4 <= EPI_BYTES) ? BM / 2 : (BM / 4 * LDT * 4 <= EPI_BYTES) ? BM / 4 : BM / 8;
     static_assert(PR * LDT * 4 <= EPI_BYTES && BM % PR == 0, "fp32 tile passes fit the stage buffers");
