@@ -181,8 +181,8 @@ __device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16
 // PIPE_DMA: the K tiles bypass the registers: each wave's 16-byte loads land
 // in LDS directly (global_load_lds_dwordx4, the 64 lanes' data in 64
 // consecutive slots, which are the same swizzled slots as above), in a ring of
-// D stages; tile kt+D-1 is in flight while tile kt is multiplied, and no
-// VGPRs are spent on staging. Each stage is an array of its own: the compiler
+// D stages: tile kt+D-1 is in flight while tile kt is multiplied, and no VGPRs
+// are spent on staging, which leaves room for 256x256 tiles. Each stage is an array of its own: the compiler
 // tracks LDS written by these loads per object, and with one array it would
 // wait for every load in flight before each LDS read of the tile.
 //
@@ -212,7 +212,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
 
     constexpr bool DMA = (FLAGS & PIPE_DMA) != 0;
     constexpr int NBUF = DMA ? D : 2;  // LDS stages per K group
-    static_assert(!DMA || (KS == 1 && D >= 3 && (D - 2) * (LA + LW) < 64), "direct-to-LDS ring");
+    static_assert(!DMA || (KS == 1 && D >= 2 && (D - 2) * (LA + LW) < 64), "direct-to-LDS ring");
     __shared__ __attribute__((aligned(16))) char smem_all[DMA ? 16 : KS * NBUF * STAGE];
     // PIPE_DMA: each stage its own array, so that the compiler sees a stage's LDS reads and
     // another stage's global->LDS loads as distinct objects and waits for neither
@@ -743,11 +743,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                     if (g.qkn_mask)
                         return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 128, 128, 2, 2, 2, 32>(gs, s)
                                    : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_QKNORM, 64, 64, 2, 2, D, 16>(gs, s);
-                    // a stack's chunked projections (65536 rows): four waves side by side,
-                    // 579 us per chunk against 637 with 2x2 waves (at 1M rows 2x2 stays ahead)
-                    if (big && gs.max_m <= 131072)
-                        return run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 1, 4, 2, 32>(gs, s);
-                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
+                    // tall products (N*B rows, and a stack's chunks of 65536): 256x256 tiles, eight
+                    // waves of 128x64, K tiles straight into two LDS stages: 601 us per chunk against
+                    // 702 for 128x128 with four waves side by side, 7.85 ms at 1M rows against 9.05
+                    // for 2x2 waves (256x256 with register staging spills)
+                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
                                : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
                 }
                 if (g.qkn_mask)
