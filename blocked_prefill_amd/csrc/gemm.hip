@@ -762,7 +762,10 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (skinny) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 16, 32, 1, 1, D, 16, KS>(gs, s);
             }
             if constexpr (KS == 1) {
-                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
+                // every tall product (N*B rows) takes the 256x256 direct-to-LDS tiles the tall
+                // q|k'|v' projection uses: a Transformer layer's forward at B=512 drops 3-4%
+                // (19.7 against 20.6 ms at N=1024), the RT layer's backward 0.5%
+                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
                 if (grouped) {
                     // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 17.4 us against 19.3
                     if constexpr (D == 4)
@@ -783,7 +786,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 4, 2, 2, 32>(gs, s);
                 // one layer's per-position product: 128x64 with eight waves of 32x32
                 // (11.4 us against 13.1 for 64x64 with four waves, M = 512)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 64, 4, 2, 2, 32>(gs, s);
             }
             break;
@@ -792,7 +795,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (skinny) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 16, 32, 1, 1, D, 16, KS>(gs, s);
             }
             if constexpr (KS == 1) {
-                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
+                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
                 if (grouped) {
                     // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 40.4-40.8 us against
                     // 44.9-45.1 (the weight and A fetches from outside L2 halve: 66 MB against 126)
@@ -835,7 +838,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             break;
         case GemmKind::W1_PRE:
             if constexpr (KS == 1)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
             break;
         case GemmKind::W2_BWD:
@@ -852,7 +855,7 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
-                if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(gs, s);
+                if (big) return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
             }
             // per-position adjoint products (M = 512, N = 1024): 64x32 tiles, twice the
             // workgroups of 64x64 (K = 1024: 6.1 against 6.9 us, 2048: 8.6 against 9.9,
