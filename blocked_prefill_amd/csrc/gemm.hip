@@ -708,6 +708,10 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     const GemmArgs& g = gs.g[0];  // the shape and flags every product of the set shares
     const bool big = gs.max_m >= 4096;
     const bool grouped = !big && gs.n >= 2;
+    // 256-column tiles need whole tiles inside every output segment (a 128-wide
+    // remainder takes the 128x128 tiles)
+    const bool wide = g.N % 256 == 0 && g.seg_n % 256 == 0;
+    const bool tall = big && wide;
     // at most 16 rows (a small batch, a decode step): 16-row tiles, 32 columns
     // wide, K split over 2 or 4 wave groups (M = 8: W_o 4.3 us against 5.9 with
     // the 64-row tiles, W_1 4.6 against 7.6, W_2 8.2 against 12.2, W_kv 4.3
@@ -747,7 +751,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                     // waves of 128x64, K tiles straight into two LDS stages: 601 us per chunk against
                     // 702 for 128x128 with four waves side by side, 7.85 ms at 1M rows against 9.05
                     // for 2x2 waves (256x256 with register staging spills)
-                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
+                    if (tall) return run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                    return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
                                : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
                 }
                 if (g.qkn_mask)
@@ -765,7 +770,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 // every tall product (N*B rows) takes the 256x256 direct-to-LDS tiles the tall
                 // q|k'|v' projection uses: a Transformer layer's forward at B=512 drops 3-4%
                 // (19.7 against 20.6 ms at N=1024), the RT layer's backward 0.5%
-                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (tall) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (big) return run_pipe<float, bf16, EPI_RESID | EPI_COPY | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
                 if (grouped) {
                     // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 17.4 us against 19.3
                     if constexpr (D == 4)
@@ -786,7 +792,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (grouped) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 4, 2, 2, 32>(gs, s);
                 // one layer's per-position product: 128x64 with eight waves of 32x32
                 // (11.4 us against 13.1 for 64x64 with four waves, M = 512)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
+                if (tall) return run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 128, 2, 2, 2, 32>(gs, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS | EPI_GELU, 128, 64, 4, 2, 2, 32>(gs, s);
             }
             break;
@@ -795,7 +802,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (skinny) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 16, 32, 1, 1, D, 16, KS>(gs, s);
             }
             if constexpr (KS == 1) {
-                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (tall) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (big) return run_pipe<bf16, float, EPI_RESID | EPI_ROWSS, 128, 128, 2, 2, 2, 32>(gs, s);
                 if (grouped) {
                     // K tiles straight into a 4-stage LDS ring, XCD-grouped tiles: 40.4-40.8 us against
                     // 44.9-45.1 (the weight and A fetches from outside L2 halve: 66 MB against 126)
@@ -837,9 +845,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             break;
         case GemmKind::W1_PRE:
-            if constexpr (KS == 1)
-                return big ? run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s)
+            if constexpr (KS == 1) {
+                if (tall) return run_pipe<bf16, float, EPI_RMS_PARTS | PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                return big ? run_pipe<bf16, float, EPI_RMS_PARTS, 128, 128, 2, 2, 2, 32>(gs, s)
                            : run_pipe<bf16, float, EPI_RMS_PARTS, 64, 64, 2, 2, D, 16>(gs, s);
+            }
             break;
         case GemmKind::W2_BWD:
             if constexpr (KS == 1) {  // 128x64 with eight waves: 11.1 us against 12.0 for 64x64 (M = 512)
@@ -850,12 +860,20 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
         case GemmKind::WGRAD:  // K of 10^4..10^6 rows per product: 128x128 tiles, eight waves of 32x64
             // K tiles straight into a 4-stage LDS ring where the K range divides into 4-tile groups
             // (the layer backward at B=512, N=2048: 393.7 ms against 403.7 with register staging)
+            // gradients of 4M entries (W_1, W_2 at d = 1024, F = 4096): 256x256 tiles with two LDS
+            // stages (64 tiles x 8 K ranges = 512 workgroups; the backward 375-377 against 387-389 ms;
+            // 256x128 for the d x d gradients as well: no further gain)
+            if constexpr (KS == 1) {
+                if ((int64_t)g.M * g.N >= ((int64_t)4 << 20) && wide)
+                    return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+            }
             if constexpr (KS == 1 && D == 4) return run_pipe<float, float, PIPE_DMA, 128, 128, 4, 2, 4, 32>(gs, s);
             if constexpr (KS == 1) return run_pipe<float, float, 0, 128, 128, 4, 2, 2, 32>(gs, s);
             break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
-                if (big) return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (tall) return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
+                if (big) return run_pipe<float, float, 0, 128, 128, 2, 2, 2, 32>(gs, s);
             }
             // per-position adjoint products (M = 512, N = 1024): 64x32 tiles, twice the
             // workgroups of 64x64 (K = 1024: 6.1 against 6.9 us, 2048: 8.6 against 9.9,

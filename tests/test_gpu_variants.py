@@ -52,19 +52,27 @@ def _forward(desc, x, w, dt):
 # ---------------------------------------------------------------- naive schedule
 
 @pytest.mark.parametrize("dt,n,b,d,h,f", [("bf16", 100, 3, 256, 4, 512), ("f32", 45, 2, 96, 3, 128),
-                                           ("bf16", 70, 2, 256, 8, 256)])
+                                           ("bf16", 70, 2, 256, 8, 256), ("bf16", 256, 16, 384, 6, 768)])
 def test_naive_schedule_layer_matches_oracle(dt, n, b, d, h, f):
     """Query t+1 reads pairs 1..t in one pass (position counts below and above
-    the MFMA kernel's 32, ragged tails); same result as the blocked schedule."""
+    the MFMA kernel's 32, ragged tails); same result as the blocked schedule.
+    At N*B = 4096 rows with d = 384 the up-front projection is a tall product
+    whose 384-column segments are not whole 256-column tiles. bf16 results are
+    held to the bar with the oracle's own noise floor over the recurrence
+    (oracle_with_floor), as every bf16 layer test of tens of positions or more."""
     x = _input(n, n, b, d, dt)
     w = _weights(n + 1, d, f, dt)
     scale = 1.0 / math.sqrt(d // h)
     naive = _forward(G.layer_desc(b, n, d, h, f, dt, scale, flags=rt.RT_FLAG_NAIVE_SCHEDULE), x, w, dt)
     blocked = _forward(G.layer_desc(b, n, d, h, f, dt, scale), x, w, dt)
-    ref = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale, round_bf16=(dt == "bf16"))
+    if dt == "bf16":
+        ref, floor = G.oracle_with_floor(x, w, n_heads=h, softmax_scale=scale)
+    else:
+        ref, floor = oracle.layer_forward(x, w, n_heads=h, softmax_scale=scale), {}
     for name in ("z", "k", "v"):
-        G.parity(G.host(getattr(naive, name)), ref[name], dt, f"naive.{name}")
-        G.parity(G.host(getattr(blocked, name)), ref[name], dt, f"blocked.{name}")
+        m = G.parity(G.host(getattr(naive, name)), ref[name], dt, f"naive.{name}", floor=floor.get(name))
+        G.parity(G.host(getattr(blocked, name)), ref[name], dt, f"blocked.{name}", floor=floor.get(name))
+        print(f"naive {dt} N={n} B={b} d={d}: {name} {m}")
 
 
 # ---------------------------------------------------------------- standard Transformer layer
@@ -72,6 +80,7 @@ def test_naive_schedule_layer_matches_oracle(dt, n, b, d, h, f):
 @pytest.mark.parametrize("dt,n,b,d,h,f", [
     ("bf16", 300, 2, 256, 4, 512),   # MFMA causal attention: 3 query tiles of 128, ragged last tile
     ("bf16", 512, 8, 256, 4, 512),   # N*B = 4096 rows: the tall-GEMM tiles
+    ("bf16", 256, 16, 384, 6, 768),  # 384-column outputs (q|k|v segments, W_o, W_2): 128-wide tall tiles
     ("bf16", 77, 3, 256, 8, 384),    # head_dim 32: SIMT causal attention
     ("f32", 60, 2, 96, 3, 128),
 ])
