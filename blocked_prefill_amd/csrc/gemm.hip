@@ -191,8 +191,11 @@ __device__ __forceinline__ void fused_small_step(const UpdateArgs& a, const bf16
 // buffers, and the KS partial tiles are added in LDS before the epilogue. At
 // the per-position shapes (M = batch) this multiplies the waves per tile and
 // divides the serial K-loop length without any cross-workgroup reduction.
+// k_off, c_off (elements): where A and W start along K and where C starts, beyond
+// the argument set's own pointers (one K range of a split product).
 template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF, int KS>
-__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t bx, const uint32_t by) {
+__device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t bx, const uint32_t by,
+                                               const int64_t k_off = 0, const int64_t c_off = 0) {
     // MF = 32: v_mfma_f32_32x32x16_bf16 blocks; MF = 16: v_mfma_f32_16x16x32_bf16 blocks
     // (four times as many independent accumulators for the same wave tile).
     static_assert(MF == 32 || MF == 16, "MFMA block");
@@ -247,8 +250,8 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     const int seg = PAIRED ? 0 : n0 / g.seg_n;
     const int pcol = (n0 / BN) * HB;  // PAIRED: first column of this tile in each segment
     const int64_t ldw = g.ldw ? g.ldw : g.K;  // row stride of W
-    const bf16* W = (const bf16*)g.W[seg] + (int64_t)(n0 % g.seg_n) * ldw;
-    const bf16* A = (const bf16*)g.A;
+    const bf16* W = (const bf16*)g.W[seg] + k_off + (int64_t)(n0 % g.seg_n) * ldw;
+    const bf16* A = (const bf16*)g.A + k_off;
 
     // this thread's chunks: slot s = NTG*i + gtid, tile row s/8, chunk column (s%8) ^ ((row/2)%8)
     const bf16* a_src[LA];
@@ -265,7 +268,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
         const int s = NTG * i + gtid, r = s >> 3, c = (s & 7) ^ ((r >> 1) & 7);
-        w_src[i] = PAIRED ? (const bf16*)g.W[r >= HB] + (int64_t)(pcol + r % HB) * ldw + c * 8
+        w_src[i] = PAIRED ? (const bf16*)g.W[r >= HB] + k_off + (int64_t)(pcol + r % HB) * ldw + c * 8
                           : W + (int64_t)r * ldw + c * 8;
     }
 
@@ -489,7 +492,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
     static_assert(!(FLAGS & EPI_ROWSS) || (BN % kRowSSTile == 0 && CPRW >= 4), "32-column groups");
     float* tl = reinterpret_cast<float*>(DMA ? stg0 : smem);          // this group's partial tile
     const float* tl0 = reinterpret_cast<const float*>(DMA ? stg0 : smem_all);
-    TC* C = (TC*)g.C[seg];
+    TC* C = (TC*)g.C[seg] + c_off;
 #pragma unroll
     for (int pass = 0; pass < BM / PR; ++pass) {
     __syncthreads();  // the stage buffers are free (last reads done; rs ready; previous pass consumed)
@@ -569,7 +572,7 @@ __device__ __forceinline__ void gemm_pipe_body(const GemmArgs& g, const uint32_t
         }
         float stored[8];
         if (ok) {
-            TC* dst = (PAIRED ? (TC*)g.C[c0 >= HB] : C) + row * g.ldc + ocol;
+            TC* dst = (PAIRED ? (TC*)g.C[c0 >= HB] + c_off : C) + row * g.ldc + ocol;
             if constexpr (sizeof(TC) == 2) {
                 bf16x8 o;
 #pragma unroll
@@ -640,6 +643,33 @@ __global__ __launch_bounds__(64 * WM * WN * KS) void gemm_pipe_group_kernel(Gemm
     const GemmArgs& g = gg.g[bz];
     if ((int64_t)by * BM >= g.M) return;  // past this product's rows (the whole workgroup)
     gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, KS>(g, bx, by);
+}
+
+// Products that differ only in their K range, one per blockIdx.z (a weight
+// gradient's reduction over rows split into ranges, each writing its own
+// partial): product z reads A and W from column z * k_step on and writes C
+// from element z * c_step on.
+struct GemmSplitK {
+    GemmArgs g;  // product 0
+    int64_t k_step, c_step;
+};
+static_assert(sizeof(GemmSplitK) <= 3584, "kernel argument size");
+
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_pipe_splitk_kernel(GemmSplitK sk) {
+    const int64_t z = blockIdx.z;
+    gemm_pipe_body<TC, TR, FLAGS, BM, BN, WM, WN, D, MF, 1>(sk.g, blockIdx.x, blockIdx.y, z * sk.k_step,
+                                                            z * sk.c_step);
+}
+
+template <typename TC, typename TR, int FLAGS, int BM, int BN, int WM, int WN, int D, int MF = 32>
+static hipError_t run_splitk(const GemmSplitK& sk, int splits, hipStream_t s) {
+    const int64_t row_tiles = (sk.g.M + BM - 1) / BM;
+    if (row_tiles > 65535 || splits > 65535) return hipErrorInvalidConfiguration;
+    dim3 grid((uint32_t)(sk.g.N / BN), (uint32_t)row_tiles, (uint32_t)splits);
+    hipLaunchKernelGGL((gemm_pipe_splitk_kernel<TC, TR, FLAGS, BM, BN, WM, WN, D, MF>), grid, dim3(64 * WM * WN), 0,
+                       s, sk);
+    return hipGetLastError();
 }
 
 // The products of one launch: n argument sets of one kind and shape (n <= kMaxGemmGroup).
@@ -857,19 +887,6 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
             }
             if (!big) return run_pipe<bf16, bf16, EPI_DGELU, 64, 64, 2, 2, D, 16, KS>(gs, s);
             break;
-        case GemmKind::WGRAD:  // K of 10^4..10^6 rows per product: 128x128 tiles, eight waves of 32x64
-            // K tiles straight into a 4-stage LDS ring where the K range divides into 4-tile groups
-            // (the layer backward at B=512, N=2048: 393.7 ms against 403.7 with register staging)
-            // gradients of 4M entries (W_1, W_2 at d = 1024, F = 4096): 256x256 tiles with two LDS
-            // stages (64 tiles x 8 K ranges = 512 workgroups; the backward 375-377 against 387-389 ms;
-            // 256x128 for the d x d gradients as well: no further gain)
-            if constexpr (KS == 1) {
-                if ((int64_t)g.M * g.N >= ((int64_t)4 << 20) && wide)
-                    return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
-            }
-            if constexpr (KS == 1 && D == 4) return run_pipe<float, float, PIPE_DMA, 128, 128, 4, 2, 4, 32>(gs, s);
-            if constexpr (KS == 1) return run_pipe<float, float, 0, 128, 128, 4, 2, 2, 32>(gs, s);
-            break;
         case GemmKind::PLAIN:
             if constexpr (KS == 1) {
                 if (tall) return run_pipe<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(gs, s);
@@ -882,6 +899,8 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
                 if (!big) return run_pipe<float, float, 0, 64, 32, 2, 2, D, 16, KS>(gs, s);
             }
             if (!big) return run_pipe<float, float, 0, 64, 32, 2, 1, D, 16, KS>(gs, s);
+            break;
+        case GemmKind::WGRAD:  // the K ranges of a weight gradient: launch_gemm_splitk
             break;
     }
     return hipErrorInvalidValue;
@@ -988,6 +1007,31 @@ hipError_t launch_gemm_group(rt_dtype dt, GemmKind kind, const GemmArgs* gs, int
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_gemm_splitk(rt_dtype dt, GemmKind kind, const GemmArgs& g, int splits, int64_t k_step,
+                              int64_t c_step, hipStream_t s) {
+    if (kind != GemmKind::WGRAD || splits <= 0 || g.M <= 0) return hipErrorInvalidValue;
+    if (dt == RT_F32) {  // one launch per K range
+        for (int z = 0; z < splits; ++z) {
+            GemmArgs a = g;
+            a.A = (const float*)g.A + z * k_step;
+            a.W[0] = (const float*)g.W[0] + z * k_step;
+            a.C[0] = (float*)g.C[0] + z * c_step;
+            const hipError_t e = launch_gemm_f32(kind, a, s);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if ((g.K / 64) % 2 || g.N % 128 || g.seg_n != g.N) return hipErrorInvalidValue;
+    const GemmSplitK sk{g, k_step, c_step};
+    // K of 10^4..10^5 rows per range. 256x256 tiles with two LDS stages, eight waves of 128x64 (the
+    // tall products' tile): at d = 1024, F = 4096 and 16 ranges a d x d gradient is 256 workgroups,
+    // a d x F one 1024. Else 128x128 with eight waves of 32x64, the K tiles straight into a 4-stage
+    // LDS ring where the range divides into 4-tile groups.
+    if (g.N % 256 == 0 && g.M >= 256) return run_splitk<float, float, PIPE_DMA, 256, 256, 2, 4, 2, 32>(sk, splits, s);
+    if ((g.K / 64) % 4 == 0) return run_splitk<float, float, PIPE_DMA, 128, 128, 4, 2, 4, 32>(sk, splits, s);
+    return run_splitk<float, float, 0, 128, 128, 4, 2, 2, 32>(sk, splits, s);
 }
 
 // ---------------------------------------------------------------- row sums of squares

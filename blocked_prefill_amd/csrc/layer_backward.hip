@@ -307,10 +307,11 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s) {
 // runs along the rows of both operands, so both are transposed first into
 // row-major [O][Rp] and [I][Rp] copies (zero past row R, Rp a multiple of the
 // split), and the product C = A_bar^T U^T^T is the library's MFMA GEMM with
-// K = Rp, split into up to kWgradSplits K ranges run as one grouped launch
-// (at O = I = 1024 a single product has 64 output tiles; eight K ranges give
-// 512 workgroups), each writing its own fp32 partial; a last pass adds the
-// partials (and the previous gradient when accumulating) in a fixed order.
+// K = Rp, split into up to kWgradSplits K ranges run as one launch (blockIdx.z
+// picks the range; at O = I = 1024 a product has 16 output tiles of 256x256,
+// so 16 ranges give 256 workgroups), each writing its own fp32 partial; a last
+// pass adds the partials (and the previous gradient when accumulating) in a
+// fixed order.
 
 namespace {
 
@@ -394,18 +395,13 @@ hipError_t weight_grad(rt_dtype dt, const void* abar, int64_t lda, const void* u
                           : transpose_pad<float>(u, R, ldu, I, ws.tu, pl.rows_pad, s);
         if (e != hipSuccess) return e;
     }
-    const size_t es = dt == RT_BF16 ? 2 : 4;
     const int64_t kc = pl.rows_pad / pl.splits;
-    GemmArgs g[kWgradSplits];
-    for (int sp = 0; sp < pl.splits; ++sp) {
-        GemmArgs& a = g[sp];
-        a = GemmArgs{};
-        a.A = (const char*)ws.ta + sp * kc * es; a.lda = pl.rows_pad;
-        a.W[0] = (const char*)ws.tu + sp * kc * es; a.ldw = pl.rows_pad;
-        a.C[0] = ws.part + (int64_t)sp * O * I; a.ldc = I; a.seg_n = I;
-        a.M = O; a.N = I; a.K = (int32_t)kc;
-    }
-    e = launch_gemm_group(dt, GemmKind::WGRAD, g, pl.splits, s);
+    GemmArgs a{};  // K range 0; range sp starts sp * kc columns on and writes partial sp
+    a.A = ws.ta; a.lda = pl.rows_pad;
+    a.W[0] = ws.tu; a.ldw = pl.rows_pad;
+    a.C[0] = ws.part; a.ldc = I; a.seg_n = I;
+    a.M = O; a.N = I; a.K = (int32_t)kc;
+    e = launch_gemm_splitk(dt, GemmKind::WGRAD, a, pl.splits, kc, (int64_t)O * I, s);
     if (e != hipSuccess) return e;
     const int64_t n = (int64_t)O * I;
     const int64_t blocks = (n / 4 + 255) / 256;

@@ -149,6 +149,10 @@ hipError_t launch_gemm(rt_dtype dt, GemmKind kind, const GemmArgs& g, hipStream_
 // (bf16; fp32 products run one launch each).
 constexpr int kMaxGemmGroup = 8;
 hipError_t launch_gemm_group(rt_dtype dt, GemmKind kind, const GemmArgs* gs, int n, hipStream_t s);
+// `splits` products in one launch that differ only in their K range (WGRAD): product z reads A and W
+// from column z * k_step on (elements) and writes C from element z * c_step on; g is product 0.
+hipError_t launch_gemm_splitk(rt_dtype dt, GemmKind kind, const GemmArgs& g, int splits, int64_t k_step,
+                              int64_t c_step, hipStream_t s);
 // out[row][0..3] = sums of x[row][c]^2 over the four quarters of the row (D % 32 == 0); a QKV
 // product given them (rss_in, n_parts = 4) takes its RMS from them.
 hipError_t launch_row_sumsq(rt_dtype dt, const void* x, int64_t rows, int D, float* out, hipStream_t s);
@@ -181,7 +185,7 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
 // both in dt; out fp32 [O][I]; O, I multiples of 4, of 128 for bf16): both operands transposed into ws
 // (ta [O][rows_pad], tu [I][rows_pad]), the product split into `splits` K ranges (fp32 partials in ws.part,
 // splits * O * I floats), then added up. u_ready: ws.tu already holds this u (the previous call's).
-constexpr int kWgradSplits = 8;
+constexpr int kWgradSplits = 16;
 struct WgradPlan {
     int64_t rows_pad;  // R rounded up to 128 * splits
     int splits;
