@@ -2,18 +2,22 @@
 //
 // Reading note (lshu.cn/news/403416), translated paper section 2: every
 // projection acts on an RMS-normalised vector. RMS(a) * W^T equals
-// rstd(a) * (a * W^T) row by row, so the normalisation is fused: the kernel
-// accumulates sum(a^2) of its A rows while staging them (each workgroup
-// streams whole rows, K is never split) and scales the product in the
-// epilogue. Section 2.1: the MLP is W_2 GELU(W_1 .) and both branches are
-// added to the residual stream, also fused here.
+// rstd(a) * (a * W^T) row by row, so the normalisation is fused: the
+// product is scaled row by row in the epilogue, from sums of a^2 over whole
+// rows (a product that normalises never splits K). Section 2.1: the MLP is
+// W_2 GELU(W_1 .) and both branches are added to the residual stream, also
+// fused here.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 on gfx950, fp32 accumulation, K tiles
-// prefetched several tiles ahead into registers and staged through a
-// double-buffered swizzled LDS tile. In bf16 layers the RMS sums of h and z
-// come from the producing GEMM's epilogue (per-row partial sums of the
-// stored values); the up-front projection sums its own A rows. fp32 path:
-// plain SIMT, one thread per output (used by small fp32 layers).
+// bf16 path: v_mfma_f32_32x32x16_bf16 / 16x16x32_bf16 on gfx950, fp32
+// accumulation. K tiles reach a swizzled LDS tile either through registers
+// (prefetched several tiles ahead, double-buffered LDS) or directly
+// (global_load_lds into a ring of LDS stages). In bf16 layers the row sums of
+// squares come as partial sums: of h and z from the producing GEMM's
+// epilogue, of a layer input from a row pass (row_sumsq); a product given
+// none sums its own A rows while it multiplies them. A weight gradient's
+// reduction over rows runs as K ranges in one launch (launch_gemm_splitk),
+// each writing a partial. fp32 path: plain SIMT, one thread per output (used
+// by small fp32 layers).
 #include <type_traits>
 
 #include "rt_device.h"
@@ -750,10 +754,11 @@ static hipError_t dispatch_bf16(GemmKind kind, const GemmSet& gs, hipStream_t s)
     // Tiles measured on MI355X at the per-position shapes (M = batch = 512): small
     // 64-row tiles of 16x16x32 MFMAs (four independent accumulators per wave),
     // with K split over 2 or 4 wave groups where that measured faster (W_2,
-    // W_o, W_kv); products over N*B rows (the up-front projection, and every
-    // product of the Transformer layer) use 128x128, prefetching 2 K tiles
-    // ahead in the tall products with fp32 operands in the epilogue (register
-    // budget: 2 waves per SIMD). Several per-position products in one launch
+    // W_o, W_kv); products over N*B rows (the up-front projection, every
+    // product of the Transformer layer, the backward's batched products) use
+    // 256x256 tiles with the K tiles loaded straight into two LDS stages
+    // (128x128 where an output segment is not whole 256-column tiles).
+    // Several per-position products in one launch
     // (the layers of a stack) fill the chip, and larger tiles then win: for six
     // products of 512 rows, W_1 128x128 (four waves side by side, 128x32 each)
     // 44.8 us against 58.8 with the per-position tile (48.3 with 2x2 waves),
