@@ -12,6 +12,9 @@
 //   x_bar = g y_bar / r - x sum(g y_bar x) / (d r^3),   g_bar += y_bar x / r.
 // The GELU's derivative Phi(u) + u phi(u) is applied in the W_2^T product's
 // epilogue (gemm.hip).
+#include <cstdint>
+#include <type_traits>
+
 #include "rt_device.h"
 #include "rt_internal.h"
 
@@ -350,6 +353,44 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const T* src, int64_
     }
 }
 
+// The same for bf16 with 16-byte accesses both ways: a thread loads 8 columns
+// of a source row, and stores 8 consecutive source rows of one column (cols,
+// lds and rows_pad multiples of 8, both pointers 16-byte aligned; the tile's
+// LDS rows padded by 8 elements stay 16-byte aligned).
+__global__ __launch_bounds__(256) void transpose_pad_bf16x8_kernel(const bf16* src, int64_t rows, int64_t lds,
+                                                                   int cols, bf16* dst, int64_t rows_pad) {
+    constexpr int PITCH = 64 + 8;
+    __shared__ __attribute__((aligned(16))) bf16 tile[64 * PITCH];
+    const int64_t r0 = (int64_t)blockIdx.y * 64;
+    const int c0 = blockIdx.x * 64;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = tid + 256 * it, rl = q >> 3, ch = (q & 7) * 8;  // tile row, first column of the run
+        const int64_t r = r0 + rl;
+        const int c = c0 + ch;
+        bf16x8 v;
+        if (r < rows && c < cols) {
+            v = *reinterpret_cast<const bf16x8*>(src + r * lds + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (bf16)0.f;
+        }
+        *reinterpret_cast<bf16x8*>(&tile[rl * PITCH + ch]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int q = tid + 256 * it, cl = q >> 3, rr = (q & 7) * 8;  // destination row, first of 8 source rows
+        const int c = c0 + cl;
+        if (c >= cols) continue;
+        bf16x8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = tile[(rr + e) * PITCH + cl];
+        *reinterpret_cast<bf16x8*>(dst + (int64_t)c * rows_pad + r0 + rr) = v;
+    }
+}
+
 // out[i] = (accumulate ? out[i] : 0) + sum_s part[s][i], s in order (n % 4 == 0).
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* part, int splits, int64_t n, float* out,
                                                            int accumulate) {
@@ -368,8 +409,13 @@ hipError_t transpose_pad(const void* src, int64_t rows, int64_t lds, int cols, v
                          hipStream_t s) {
     if (cols % 4 || rows_pad % 64 || rows_pad / 64 > 65535) return hipErrorInvalidValue;
     const dim3 grid((uint32_t)((cols + 63) / 64), (uint32_t)(rows_pad / 64));
-    hipLaunchKernelGGL(transpose_pad_kernel<T>, grid, dim3(256), 0, s, (const T*)src, rows, lds, cols, (T*)dst,
-                       rows_pad);
+    if (std::is_same<T, bf16>::value && cols % 8 == 0 && lds % 8 == 0 && (uintptr_t)src % 16 == 0 &&
+        (uintptr_t)dst % 16 == 0)
+        hipLaunchKernelGGL(transpose_pad_bf16x8_kernel, grid, dim3(256), 0, s, (const bf16*)src, rows, lds, cols,
+                           (bf16*)dst, rows_pad);
+    else
+        hipLaunchKernelGGL(transpose_pad_kernel<T>, grid, dim3(256), 0, s, (const T*)src, rows, lds, cols, (T*)dst,
+                           rows_pad);
     return hipGetLastError();
 }
 

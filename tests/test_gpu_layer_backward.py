@@ -89,6 +89,9 @@ def _run(dt, n, b, d, heads, f, rho, gains, seed):
     ("f32", 20, 2, 64, 2, 128, 0.7, True),
     ("bf16", 100, 3, 256, 4, 512, 1.0, True),
     ("bf16", 64, 64, 256, 4, 512, 0.8, False),   # N*B = 4096 rows: the batched products' tall tiles
+    # N*B = 16384 rows: the weight gradients in 16 K ranges of one launch, on 256x256 tiles where the
+    # gradient has 256-column multiples (W_2's 384 x 768) and 128x128 where not (d = 384)
+    ("bf16", 64, 256, 384, 6, 768, 0.9, False),
 ])
 def test_layer_backward_matches_oracle(dt, n, b, d, heads, f, rho, gains):
     got, ref = _run(dt, n, b, d, heads, f, rho, gains, seed=500 + n)
